@@ -1,0 +1,156 @@
+"""Split plan: a plain reference of the cut rule, and its invariants.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+The FlashMLA backend page (``init_forward_metadata``, ``get_mla_metadata``
+call) only fixes the shapes of the plan: a tile-scheduler table of
+``[num_sm_parts, 8]`` int32 with num_sm_parts at most the multiprocessor
+count (the assert in ``_apply_decode_target_verify_metadata``) and a
+``num_splits`` vector of length bs+1.  The planning rule itself is not on the
+pages, and several plans are correct.  What every correct plan satisfies is
+checked by :func:`check_plan`; :func:`plan_reference` writes out the one rule
+this library documents, so that the device planner can also be compared
+exactly.
+
+The rule.  Request b has N_b = ceil(L_b / 64) pages and costs N_b + c page
+units, c = plan_overhead(rows) (0 when N_b = 0); C is the total cost and
+T = ceil(C / parts).  A position x inside
+request b (cum_b <= x < cum_b + cost_b) maps to the flattened page index
+pagecum_b + clamp(x - cum_b - c, 0, N_b); the first c units of a request are
+its fixed overhead.  With x_p = floor(p*C / parts), part p owns flattened
+pages [G(x_p), G(x_{p+1})), so every part spans at most T cost units.
+
+Table row (8 int32): begin_req, begin_page, end_req (inclusive),
+end_page (exclusive, inside end_req), piece index of the first piece inside
+begin_req, number of pages, 0, 0.  An empty part has 0 pages and zeros
+elsewhere.  split_indptr[b] counts the pieces before request b; a request's
+pieces are the parts that touch it, in part order.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+PAGE_SIZE = 64
+
+
+def plan_overhead(rows_per_req: int) -> int:
+    """Fixed per-piece cost in page units: loading q and writing the result
+    of ``rows_per_req`` rows (about one page per 64 rows), plus one."""
+    return 1 + rows_per_req // 64
+
+
+def _locate(g: int, pagecum: np.ndarray, npages: np.ndarray):
+    """Flattened page index g -> (request, page) for a page that exists."""
+    b = int(np.searchsorted(pagecum, g, side="right") - 1)
+    while npages[b] == 0 or g >= pagecum[b] + npages[b]:
+        b += 1
+    return b, g - int(pagecum[b])
+
+
+def plan_reference(seq_lens, num_parts: int, rows_per_req: int):
+    L = np.asarray(seq_lens, dtype=np.int64)
+    bs = len(L)
+    c = plan_overhead(rows_per_req)
+    npages = -(-L // PAGE_SIZE)
+    cost = np.where(npages > 0, npages + c, 0)
+    cum = np.concatenate([[0], np.cumsum(cost)])
+    pagecum = np.concatenate([[0], np.cumsum(npages)])
+    C = int(cum[-1])
+    T = max(1, -(-C // num_parts))
+
+    def G(x: int) -> int:
+        if x >= C:
+            return int(pagecum[-1])
+        b = int(np.searchsorted(cum, x, side="right") - 1)
+        o = x - int(cum[b])
+        return int(pagecum[b]) + int(min(max(o - c, 0), npages[b]))
+
+    cuts = [G(p * C // num_parts) for p in range(num_parts + 1)]
+    cuts[num_parts] = int(pagecum[-1])
+
+    # interior cut positions, distinct, per request
+    interior = set()
+    for g in cuts[1:num_parts]:
+        if 0 < g < pagecum[-1]:
+            b, pg = _locate(g, pagecum, npages)
+            if pg > 0:
+                interior.add(g)
+    pieces = np.zeros(bs, dtype=np.int64)
+    for b in range(bs):
+        if npages[b] == 0:
+            continue
+        lo, hi = int(pagecum[b]), int(pagecum[b] + npages[b])
+        pieces[b] = 1 + sum(1 for g in interior if lo < g < hi)
+    indptr = np.concatenate([[0], np.cumsum(pieces)]).astype(np.int32)
+
+    table = np.zeros((num_parts, 8), dtype=np.int32)
+    for p in range(num_parts):
+        g0, g1 = cuts[p], cuts[p + 1]
+        if g1 <= g0:
+            continue
+        b0, pg0 = _locate(g0, pagecum, npages)
+        b1, pg1 = _locate(g1 - 1, pagecum, npages)
+        first_idx = sum(1 for g in interior if pagecum[b0] < g <= g0)
+        table[p] = [b0, pg0, b1, pg1 + 1, first_idx, g1 - g0, 0, 0]
+    return table, indptr
+
+
+def check_plan(table, indptr, seq_lens, num_parts: int, rows_per_req: int) -> None:
+    """Raise AssertionError unless (table, indptr) is a correct plan:
+
+    * shapes [num_parts, 8] and [bs+1]; indptr[0] = 0, non-decreasing,
+      indptr[bs] <= bs + num_parts;
+    * every page of every request lies in exactly one part, parts are
+      page-aligned ranges of the (request, page) sequence in order;
+    * request b has indptr[b+1]-indptr[b] pieces, one per part touching it,
+      numbered 0.. in part order (the first one given by field 4);
+    * each part costs at most ceil(total cost / num_parts) + c page units.
+    """
+    table = np.asarray(table)
+    indptr = np.asarray(indptr, dtype=np.int64)
+    L = np.asarray(seq_lens, dtype=np.int64)
+    bs = len(L)
+    c = plan_overhead(rows_per_req)
+    assert table.shape == (num_parts, 8), table.shape
+    assert indptr.shape == (bs + 1,), indptr.shape
+    assert indptr[0] == 0
+    assert np.all(np.diff(indptr) >= 0)
+    assert indptr[-1] <= bs + num_parts
+    npages = -(-L // PAGE_SIZE)
+    C = int(np.where(npages > 0, npages + c, 0).sum())
+    T = max(1, -(-C // num_parts))
+
+    seen = [np.zeros(int(n), dtype=np.int64) for n in npages]
+    pieces_seen = [[] for _ in range(bs)]
+    last = (0, 0)  # next (request, page) expected, in order
+    for p in range(num_parts):
+        b0, pg0, b1, pg1, first_idx, npg, r0, r1 = [int(v) for v in table[p]]
+        assert r0 == 0 and r1 == 0
+        if npg == 0:
+            assert (b0, pg0, b1, pg1, first_idx) == (0, 0, 0, 0, 0), table[p]
+            continue
+        assert 0 <= b0 <= b1 < bs, table[p]
+        assert (b0, pg0) >= last, f"part {p} out of order"
+        count = 0
+        cost = 0
+        for b in range(b0, b1 + 1):
+            lo = pg0 if b == b0 else 0
+            hi = pg1 if b == b1 else int(npages[b])
+            assert 0 <= lo <= hi <= npages[b], table[p]
+            if hi == lo:
+                continue
+            seen[b][lo:hi] += 1
+            idx = first_idx if b == b0 else 0
+            pieces_seen[b].append((p, idx, lo, hi))
+            count += hi - lo
+            cost += hi - lo + c
+        assert count == npg, table[p]
+        assert cost <= T + c, f"part {p} cost {cost} > {T} + {c}"
+        last = (b1, pg1)
+    for b in range(bs):
+        assert np.all(seen[b] == 1), f"request {b} pages not covered exactly once"
+        k = int(indptr[b + 1] - indptr[b])
+        assert k == len(pieces_seen[b]), f"request {b}: {k} pieces declared, {len(pieces_seen[b])} found"
+        for j, (_, idx, _, _) in enumerate(pieces_seen[b]):
+            assert idx == j, f"request {b}: piece numbering"
