@@ -1,0 +1,220 @@
+/*
+ * mla_decode.h — C ABI of the MI355X (gfx950) MLA paged-KV decode library.
+ *
+ * The library computes batched decode attention in the multi-head latent
+ * attention (MLA) "absorbed" form over a paged latent cache, as the FlashMLA
+ * attention backend page of SGLang drives it:
+ *
+ *   - q is [bs, q_len, H, 576] (kv_lora_rank 512 + rope 64), viewed that way
+ *     in FlashMLABackend.forward_decode;
+ *   - the cache is [num_pages, 64, 576] latent rows (64-token pages, the
+ *     module's PAGE_SIZE; forward_decode views it as [-1, 64, 1, 576]);
+ *     V is the first 512 columns of the same row (head_dim_v = kv_lora_rank);
+ *   - pages are found through a per-request block table built from the
+ *     req_to_token map (init_forward_metadata);
+ *   - the KV sequence is split into pieces by a planner (the get_mla_metadata
+ *     call: a [num_parts, 8] tile table and a bs+1 split vector), each piece
+ *     produces a partial (o, lse) state, and the pieces are merged exactly
+ *     (the merge_state step of the FlashInfer backend page's forward_extend).
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer is device memory unless its comment says "host".
+ *   - The caller owns every buffer.  The library allocates no device memory
+ *     and keeps no state between calls apart from a thread-local error text.
+ *   - Calls are asynchronous on the given HIP stream (0 = the null stream),
+ *     never synchronise and never read device memory on the host, so they can
+ *     be captured in a HIP graph (the FlashMLA page prepares fixed-capacity
+ *     buffers for graph replay in init_cuda_graph_state).
+ *   - Argument errors are detected on the host before any launch and
+ *     returned as a status; nothing is launched then.  No C++ exception
+ *     crosses the ABI; no call aborts the process.
+ *   - Row order inside a request is r = i*H + h (token i of q_len, head h).
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+#define MLA_PAGE_SIZE 64
+#define MLA_LATENT_DIM 576
+#define MLA_V_DIM 512
+#define MLA_MAX_ROWS_PER_REQ 512   /* H * q_len */
+#define MLA_MAX_BATCH 16384        /* planner limit */
+#define MLA_MAX_PARTS 512          /* planner limit (also <= device CU count) */
+
+typedef enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, bad enum, non-finite scale */
+  MLA_ERR_UNSUPPORTED = 2,      /* a shape or dtype this build has no kernel for */
+  MLA_ERR_CAPACITY = 3,         /* a caller buffer is too small for the request */
+  MLA_ERR_PRECONDITION = 4,     /* reserved for debug builds */
+  MLA_ERR_DEVICE = 5            /* a HIP runtime call failed; see mla_last_error_message */
+} mla_status;
+
+typedef enum mla_kv_dtype {
+  MLA_KV_BF16 = 0,      /* latent rows are bf16 */
+  MLA_KV_FP8_E4M3 = 1   /* latent rows are OCP float8 e4m3fn bytes, times a per-tensor descale */
+} mla_kv_dtype;
+
+/* Version of this ABI (MLA_ABI_VERSION of the build). */
+int32_t mla_abi_version(void);
+
+/* Static text for a status code. */
+const char* mla_status_string(mla_status status);
+
+/* Text describing the last non-OK status returned on this host thread
+ * ("" if none).  Valid until the next library call on the thread. */
+const char* mla_last_error_message(void);
+
+/*
+ * mla_build_block_table — per-request page table.
+ *
+ * The index kernel the FlashMLA page launches in init_forward_metadata
+ * (create_flashmla_kv_indices_triton, body not on the page): for request b,
+ * n_b = ceil(seq_lens[b] / 64) and, for p < n_b,
+ *     block_table[b * bt_row_stride + p] = floor(req_to_token[rpi[b] * r2t_row_stride + 64*p] / 64)
+ * i.e. the page holding token 64p.  Every other cell of the row, up to
+ * bt_row_stride, is written with pad_value (the page pre-fills with -1).
+ * Slots are assumed page-aligned (slot of token j = 64*page + j % 64).
+ *
+ *   req_to_token      int32 [r2t_rows, r2t_row_stride]
+ *   req_pool_indices  int32 [bs], each in [0, r2t_rows)
+ *   seq_lens          int32 [bs], KV lengths incl. the new tokens, >= 0
+ *   page_size         must be 64
+ *   block_table       int32 [bs, bt_row_stride], written in full
+ *   max_seq_len_hint  host: an upper bound of seq_lens, or -1 if unknown
+ *
+ * Errors: INVALID_ARGUMENT for null pointers, bs <= 0, r2t_rows <= 0,
+ * bt_row_stride <= 0 or r2t_row_stride <= 0; UNSUPPORTED for page_size != 64;
+ * CAPACITY when the hint needs more than bt_row_stride pages or more than
+ * r2t_row_stride slots.  Without a hint the device clamps a request that needs
+ * more than bt_row_stride pages to bt_row_stride pages, and a cell whose
+ * req_to_token read would fall outside the map gets pad_value.
+ */
+mla_status mla_build_block_table(const int32_t* req_to_token, int32_t r2t_rows,
+                                 int64_t r2t_row_stride, const int32_t* req_pool_indices,
+                                 const int32_t* seq_lens, int32_t bs, int32_t page_size,
+                                 int32_t* block_table, int32_t bt_row_stride,
+                                 int32_t pad_value, int32_t max_seq_len_hint,
+                                 hipStream_t stream);
+
+/*
+ * mla_plan_splits — split the (request, page) sequence over num_parts
+ * work-groups (the get_mla_metadata call of init_forward_metadata: a
+ * [num_parts, 8] table and a bs+1 vector; num_parts at most the CU count).
+ *
+ * Rule (deterministic, depends only on seq_lens, rows_per_req, num_parts):
+ * request b has N_b = ceil(L_b/64) pages and costs N_b + c page units, with
+ * c = 1 + rows_per_req/64 (0 for an empty request).  With C the total cost,
+ * part p covers cost positions [floor(pC/P), floor((p+1)C/P)); a position x
+ * inside request b maps to the page boundary clamp(x - cum_b - c, 0, N_b).
+ * Each part therefore costs at most ceil(C/P) + c units, every page lies in
+ * exactly one part, and the number of pieces is at most bs + num_parts.
+ *
+ *   tile_plan     int32 [num_parts, 8]: begin_req, begin_page, end_req
+ *                 (inclusive), end_page (exclusive, in end_req), piece index
+ *                 of the first piece inside begin_req, number of pages, 0, 0.
+ *                 An empty part is all zeros.
+ *   split_indptr  int32 [bs + 1]: split_indptr[b] = pieces before request b;
+ *                 request b's pieces use partial slots split_indptr[b] ..
+ *                 split_indptr[b+1]-1, in part order.
+ *   kv_dtype      MLA_KV_BF16 or MLA_KV_FP8_E4M3 (accepted for symmetry with
+ *                 the page's is_fp8_kvcache flag; the rule does not use it).
+ *
+ * Errors: INVALID_ARGUMENT for null pointers, bs <= 0, num_parts <= 0 or a bad
+ * dtype; UNSUPPORTED for rows_per_req outside 1..512; CAPACITY for
+ * bs > MLA_MAX_BATCH, num_parts > MLA_MAX_PARTS or num_parts above the current
+ * device's CU count (the page asserts num_sm_parts <= preallocated count).
+ */
+mla_status mla_plan_splits(const int32_t* seq_lens, int32_t bs, int32_t rows_per_req,
+                           int32_t num_parts, int32_t kv_dtype, int32_t* tile_plan,
+                           int32_t* split_indptr, hipStream_t stream);
+
+/* Host helpers: upper bound of split_indptr[bs] (= bs + num_parts), and the
+ * bytes of the partial_o + partial_lse buffers that bound needs. */
+int32_t mla_max_total_splits(int32_t bs, int32_t num_parts);
+size_t mla_partial_bytes(int32_t bs, int32_t rows_per_req, int32_t num_parts);
+
+/* Host helper: CU count of the current device (the default num_parts), or -1. */
+int32_t mla_device_num_cus(void);
+
+/*
+ * mla_decode — split attention over the plan's pieces
+ * (flash_mla_with_kvcache as forward_decode and the target-verify branch of
+ * forward_extend call it).
+ *
+ * For request b, query row r = i*H + h (i < q_len) and visible keys
+ * j <= L_b - q_len + i when causal (bottom-right aligned; all j < L_b
+ * otherwise), with K_j the latent row of token j (times *kv_descale for fp8)
+ * and V_j its first 512 columns:
+ *     s_j = softmax_scale * <q_r, K_j>,  lse_r = ln sum_j exp(s_j),
+ *     o_r = sum_j exp(s_j - lse_r) V_j.
+ * A piece computes these sums over its own pages.  A request with exactly
+ * one piece is final: o goes to out (bf16, round to nearest even) and lse to
+ * lse.  Otherwise each piece writes its (o, lse) in fp32 to partial slot
+ * split_indptr[b] + piece, and mla_merge_states finishes the request.
+ *
+ *   q             bf16 [bs, q_len, num_heads, 576], contiguous
+ *   kv_cache      [num_pages, 64, 576] bf16, or bytes for MLA_KV_FP8_E4M3
+ *   block_table   int32 [bs, bt_row_stride] from mla_build_block_table
+ *   seq_lens      int32 [bs], the lengths the plan was made from
+ *   tile_plan, split_indptr, num_parts   from mla_plan_splits
+ *   softmax_scale host, by value (passed as a host float so no device read is
+ *                 needed, as the FlashInfer page notes for graph capture)
+ *   kv_descale    device fp32 scalar for fp8 (NULL for bf16)
+ *   partial_o     fp32 [partial_slots, q_len*num_heads, 512]
+ *   partial_lse   fp32 [partial_slots, q_len*num_heads]
+ *   out           bf16 [bs, q_len, num_heads, 512] (rows of split requests
+ *                 are written by mla_merge_states)
+ *   lse           fp32 [bs, q_len, num_heads] natural-log LSE, or NULL
+ *
+ * Block-table entries outside [0, num_pages) are a caller error; the kernel
+ * then reads page 0 instead, so it never leaves the pool.
+ *
+ * Errors: INVALID_ARGUMENT for null pointers, non-positive sizes, a
+ * non-finite scale, or fp8 with a NULL kv_descale; UNSUPPORTED for
+ * q_len*num_heads outside 1..512 or an unknown kv_dtype; CAPACITY when
+ * partial_slots < bs + num_parts.
+ */
+mla_status mla_decode(const void* q, int32_t bs, int32_t q_len, int32_t num_heads,
+                      const void* kv_cache, int32_t kv_dtype, int64_t num_pages,
+                      const int32_t* block_table, int32_t bt_row_stride,
+                      const int32_t* seq_lens, const int32_t* tile_plan, int32_t num_parts,
+                      const int32_t* split_indptr, float softmax_scale, int32_t causal,
+                      const float* kv_descale, float* partial_o, float* partial_lse,
+                      int32_t partial_slots, void* out, float* lse, hipStream_t stream);
+
+/*
+ * mla_merge_states — exact merge of partial (o, lse) states (merge_state of
+ * the FlashInfer page's forward_extend, generalised to k pieces).
+ *
+ * For request b with k = split_indptr[b+1] - split_indptr[b] pieces and each
+ * row r:  M = max_k lse_k,  LSE = M + ln sum_k exp(lse_k - M),
+ *         o = sum_k exp(lse_k - LSE) * o_k.
+ * Pieces with lse = -inf weigh 0; if all do, o = 0 and LSE = -inf.
+ * k == 1: the request is skipped (mla_decode already wrote it).
+ * k == 0: o = 0 and LSE = -inf are written.
+ * A two-way merge of arbitrary states is the case split_indptr = {0, 2, 4, ...}.
+ *
+ *   partial_o     fp32 [slots, rows_per_req, 512];  partial_lse fp32 [slots, rows_per_req]
+ *   out           bf16 [bs, rows_per_req, 512];     lse fp32 [bs, rows_per_req] or NULL
+ *
+ * Errors: INVALID_ARGUMENT for null pointers or bs <= 0; UNSUPPORTED for
+ * rows_per_req outside 1..512.
+ */
+mla_status mla_merge_states(const float* partial_o, const float* partial_lse,
+                            const int32_t* split_indptr, int32_t bs, int32_t rows_per_req,
+                            void* out, float* lse, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

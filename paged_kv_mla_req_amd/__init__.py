@@ -1,0 +1,203 @@
+"""MI355X (gfx950) MLA paged-KV decode: thin Python binding of the C ABI.
+
+Every function here only checks tensor shapes/dtypes/devices, takes raw
+device pointers and the current HIP stream, and calls the same-named entry
+point of ``libmla_decode.so`` (declared in ``include/mla_decode.h``).  All
+arithmetic runs in the library's HIP kernels; nothing falls back to torch or
+to the CPU.  PyTorch is used for device memory and streams only.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import MLAError, MLA_KV_BF16, MLA_KV_FP8_E4M3  # noqa: F401
+
+PAGE_SIZE = 64
+LATENT_DIM = 576
+V_DIM = 512
+
+_KV_DTYPES = {"bf16": MLA_KV_BF16, "fp8_e4m3": MLA_KV_FP8_E4M3}
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtypes, ndim: Optional[int] = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def _kv_code(kv_dtype) -> int:
+    if isinstance(kv_dtype, int):
+        return kv_dtype
+    try:
+        return _KV_DTYPES[kv_dtype]
+    except KeyError:
+        raise ValueError(f"unknown kv_dtype {kv_dtype!r}") from None
+
+
+def abi_version() -> int:
+    return int(_lib.lib().mla_abi_version())
+
+
+def device_num_cus() -> int:
+    return int(_lib.lib().mla_device_num_cus())
+
+
+def max_total_splits(bs: int, num_parts: int) -> int:
+    return int(_lib.lib().mla_max_total_splits(bs, num_parts))
+
+
+def build_block_table(req_to_token: torch.Tensor, req_pool_indices: torch.Tensor,
+                      seq_lens: torch.Tensor, width: int, pad_value: int = -1,
+                      max_seq_len_hint: int = -1, out: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """int32 [bs, width] block table (mla_build_block_table)."""
+    _need(req_to_token, "req_to_token", (torch.int32,), 2)
+    _need(req_pool_indices, "req_pool_indices", (torch.int32,), 1)
+    _need(seq_lens, "seq_lens", (torch.int32,), 1)
+    bs = seq_lens.shape[0]
+    if out is None:
+        out = torch.empty((bs, width), dtype=torch.int32, device=seq_lens.device)
+    _need(out, "out", (torch.int32,), 2)
+    _lib.check(_lib.lib().mla_build_block_table(
+        _p(req_to_token), req_to_token.shape[0], req_to_token.stride(0), _p(req_pool_indices),
+        _p(seq_lens), bs, PAGE_SIZE, _p(out), out.shape[1], pad_value, max_seq_len_hint,
+        _stream(stream)))
+    return out
+
+
+def plan_splits(seq_lens: torch.Tensor, rows_per_req: int, num_parts: Optional[int] = None,
+                kv_dtype="bf16", tile_plan: Optional[torch.Tensor] = None,
+                split_indptr: Optional[torch.Tensor] = None,
+                stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(tile_plan int32 [num_parts, 8], split_indptr int32 [bs+1]) (mla_plan_splits).
+    ``num_parts`` defaults to the device's CU count."""
+    _need(seq_lens, "seq_lens", (torch.int32,), 1)
+    bs = seq_lens.shape[0]
+    if num_parts is None:
+        num_parts = device_num_cus()
+    if tile_plan is None:
+        tile_plan = torch.empty((num_parts, 8), dtype=torch.int32, device=seq_lens.device)
+    if split_indptr is None:
+        split_indptr = torch.empty((bs + 1,), dtype=torch.int32, device=seq_lens.device)
+    _need(tile_plan, "tile_plan", (torch.int32,), 2)
+    _need(split_indptr, "split_indptr", (torch.int32,), 1)
+    if tile_plan.shape[0] < num_parts or split_indptr.shape[0] < bs + 1:
+        raise ValueError("plan buffers too small")
+    _lib.check(_lib.lib().mla_plan_splits(_p(seq_lens), bs, rows_per_req, num_parts,
+                                          _kv_code(kv_dtype), _p(tile_plan), _p(split_indptr),
+                                          _stream(stream)))
+    return tile_plan[:num_parts], split_indptr[:bs + 1]
+
+
+def partial_buffers(bs: int, rows_per_req: int, num_parts: int,
+                    device="cuda") -> Tuple[torch.Tensor, torch.Tensor]:
+    """Workspace for split pieces: partial o fp32 [bs+num_parts, R, 512] and
+    partial lse fp32 [bs+num_parts, R]."""
+    slots = max_total_splits(bs, num_parts)
+    return (torch.empty((slots, rows_per_req, V_DIM), dtype=torch.float32, device=device),
+            torch.empty((slots, rows_per_req), dtype=torch.float32, device=device))
+
+
+def mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+               seq_lens: torch.Tensor, tile_plan: torch.Tensor, split_indptr: torch.Tensor,
+               softmax_scale: float, *, partial_o: torch.Tensor, partial_lse: torch.Tensor,
+               out: torch.Tensor, lse: Optional[torch.Tensor] = None, kv_dtype="bf16",
+               kv_descale: Optional[torch.Tensor] = None, causal: bool = True,
+               stream=None) -> None:
+    """Split attention over the plan's pieces (mla_decode)."""
+    _need(q, "q", (torch.bfloat16,), 4)
+    code = _kv_code(kv_dtype)
+    kv_ok = (torch.bfloat16, torch.int16, torch.uint16) if code == MLA_KV_BF16 else (
+        torch.uint8, torch.float8_e4m3fn)
+    _need(kv_cache, "kv_cache", kv_ok, 3)
+    if kv_cache.shape[1:] != (PAGE_SIZE, LATENT_DIM):
+        raise ValueError(f"kv_cache must be [pages, 64, 576], got {tuple(kv_cache.shape)}")
+    bs, q_len, heads, d = q.shape
+    if d != LATENT_DIM:
+        raise ValueError("q must be [bs, q_len, heads, 576]")
+    _need(block_table, "block_table", (torch.int32,), 2)
+    _need(seq_lens, "seq_lens", (torch.int32,), 1)
+    _need(tile_plan, "tile_plan", (torch.int32,), 2)
+    _need(split_indptr, "split_indptr", (torch.int32,), 1)
+    _need(partial_o, "partial_o", (torch.float32,), 3)
+    _need(partial_lse, "partial_lse", (torch.float32,), 2)
+    _need(out, "out", (torch.bfloat16,), 4)
+    if lse is not None:
+        _need(lse, "lse", (torch.float32,), 3)
+    if kv_descale is not None:
+        _need(kv_descale, "kv_descale", (torch.float32,))
+    rows = q_len * heads
+    if partial_o.shape[1:] != (rows, V_DIM) or partial_lse.shape != (partial_o.shape[0], rows):
+        raise ValueError("partial buffers do not match q")
+    _lib.check(_lib.lib().mla_decode(
+        _p(q), bs, q_len, heads, _p(kv_cache), code, kv_cache.shape[0], _p(block_table),
+        block_table.shape[1], _p(seq_lens), _p(tile_plan), tile_plan.shape[0], _p(split_indptr),
+        float(softmax_scale), 1 if causal else 0, _p(kv_descale), _p(partial_o), _p(partial_lse),
+        partial_o.shape[0], _p(out), _p(lse), _stream(stream)))
+
+
+def merge_states(partial_o: torch.Tensor, partial_lse: torch.Tensor, split_indptr: torch.Tensor,
+                 out: torch.Tensor, lse: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Exact LSE merge of split pieces into out (bf16) and lse (mla_merge_states)."""
+    _need(partial_o, "partial_o", (torch.float32,), 3)
+    _need(partial_lse, "partial_lse", (torch.float32,), 2)
+    _need(split_indptr, "split_indptr", (torch.int32,), 1)
+    _need(out, "out", (torch.bfloat16,))
+    bs = split_indptr.shape[0] - 1
+    rows = partial_o.shape[1]
+    if out.numel() != bs * rows * V_DIM:
+        raise ValueError("out does not match split_indptr and partial_o")
+    if lse is not None:
+        _need(lse, "lse", (torch.float32,))
+        if lse.numel() != bs * rows:
+            raise ValueError("lse does not match")
+    _lib.check(_lib.lib().mla_merge_states(_p(partial_o), _p(partial_lse), _p(split_indptr), bs,
+                                           rows, _p(out), _p(lse), _stream(stream)))
+
+
+def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+           seq_lens: torch.Tensor, softmax_scale: float, *, kv_dtype="bf16",
+           kv_descale: Optional[torch.Tensor] = None, causal: bool = True,
+           num_parts: Optional[int] = None, plan=None, workspace=None,
+           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+           stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """mla_decode followed by mla_merge_states; returns (out bf16 [bs, q_len, H, 512],
+    lse fp32 [bs, q_len, H]).  ``plan`` = (tile_plan, split_indptr) from plan_splits,
+    ``workspace`` = (partial_o, partial_lse) from partial_buffers."""
+    bs, q_len, heads, _ = q.shape
+    rows = q_len * heads
+    if plan is None:
+        plan = plan_splits(seq_lens, rows, num_parts, kv_dtype, stream=stream)
+    tile_plan, split_indptr = plan
+    if workspace is None:
+        workspace = partial_buffers(bs, rows, tile_plan.shape[0], q.device)
+    if out is None:
+        out = torch.empty((bs, q_len, heads, V_DIM), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((bs, q_len, heads), dtype=torch.float32, device=q.device)
+    mla_decode(q, kv_cache, block_table, seq_lens, tile_plan, split_indptr, softmax_scale,
+               partial_o=workspace[0], partial_lse=workspace[1], out=out, lse=lse,
+               kv_dtype=kv_dtype, kv_descale=kv_descale, causal=causal, stream=stream)
+    merge_states(workspace[0], workspace[1], split_indptr, out, lse, stream=stream)
+    return out, lse

@@ -1,0 +1,67 @@
+// Status codes, error text and host helpers of the C ABI.
+#include <cmath>
+#include <string>
+
+#include "common.h"
+
+namespace mla {
+
+static thread_local std::string g_last_error;
+
+mla_status fail(mla_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+mla_status ok() {
+  g_last_error.clear();
+  return MLA_OK;
+}
+
+mla_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(MLA_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace mla
+
+extern "C" {
+
+int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+const char* mla_status_string(mla_status status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported";
+    case MLA_ERR_CAPACITY: return "capacity exceeded";
+    case MLA_ERR_PRECONDITION: return "precondition violated";
+    case MLA_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char* mla_last_error_message(void) { return mla::g_last_error.c_str(); }
+
+int32_t mla_max_total_splits(int32_t bs, int32_t num_parts) {
+  if (bs < 0 || num_parts < 0) return -1;
+  return bs + num_parts;
+}
+
+size_t mla_partial_bytes(int32_t bs, int32_t rows_per_req, int32_t num_parts) {
+  if (bs < 0 || num_parts < 0 || rows_per_req < 0) return 0;
+  size_t slots = (size_t)bs + (size_t)num_parts;
+  return slots * (size_t)rows_per_req * (size_t)(MLA_V_DIM + 1) * sizeof(float);
+}
+
+int32_t mla_device_num_cus(void) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  return cus;
+}
+
+}  // extern "C"

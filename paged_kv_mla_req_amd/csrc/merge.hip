@@ -1,0 +1,84 @@
+// Exact merge of partial attention states.
+//
+// The FlashInfer backend page computes attention over two disjoint key sets
+// (ragged new tokens, paged prefix), each returning (o, lse), and combines
+// them with merge_state; the FlashMLA page returns lse so that decode
+// context-parallel ranks can correct their outputs the same way.  This kernel
+// does the k-way form for every request whose keys mla_decode split into k
+// pieces:  LSE = M + ln sum_k exp(lse_k - M),  o = sum_k exp(lse_k - LSE) o_k.
+//
+// One wave per (request, row): each lane owns 8 of the 512 value columns
+// (two 16-byte loads per piece), so a piece's row is read fully coalesced.
+// Pure HBM streaming; no MFMA.
+#include "common.h"
+
+namespace mla {
+
+constexpr int kMergeWaves = 4;
+
+__global__ void __launch_bounds__(64 * kMergeWaves)
+merge_states_kernel(const float* __restrict__ partial_o, const float* __restrict__ partial_lse,
+                    const int32_t* __restrict__ split_indptr, int bs, int rows,
+                    uint16_t* __restrict__ out, float* __restrict__ lse_out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t gw = (int64_t)blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
+  if (gw >= (int64_t)bs * rows) return;
+  const int b = (int)(gw / rows);
+  const int r = (int)(gw - (int64_t)b * rows);
+  const int k0 = split_indptr[b];
+  const int k = split_indptr[b + 1] - k0;
+  if (k == 1) return;  // already final
+
+  float4 acc0 = make_float4(0.f, 0.f, 0.f, 0.f), acc1 = acc0;
+  float LSE = -INFINITY;
+  if (k > 1) {
+    float M = -INFINITY;
+    for (int s = 0; s < k; ++s) M = fmaxf(M, partial_lse[(int64_t)(k0 + s) * rows + r]);
+    if (M != -INFINITY) {
+      float tot = 0.f;
+      for (int s = 0; s < k; ++s) {
+        float l = partial_lse[(int64_t)(k0 + s) * rows + r];
+        tot += (l == -INFINITY) ? 0.f : __expf(l - M);
+      }
+      LSE = M + __logf(tot);
+      for (int s = 0; s < k; ++s) {
+        float l = partial_lse[(int64_t)(k0 + s) * rows + r];
+        if (l == -INFINITY) continue;
+        const float w = __expf(l - LSE);
+        const float4* src = reinterpret_cast<const float4*>(
+            partial_o + ((int64_t)(k0 + s) * rows + r) * kDv) + lane * 2;
+        float4 x0 = src[0], x1 = src[1];
+        acc0.x += w * x0.x; acc0.y += w * x0.y; acc0.z += w * x0.z; acc0.w += w * x0.w;
+        acc1.x += w * x1.x; acc1.y += w * x1.y; acc1.z += w * x1.z; acc1.w += w * x1.w;
+      }
+    }
+  }
+  uint4 packed;
+  packed.x = (uint32_t)f32_to_bf16(acc0.x) | ((uint32_t)f32_to_bf16(acc0.y) << 16);
+  packed.y = (uint32_t)f32_to_bf16(acc0.z) | ((uint32_t)f32_to_bf16(acc0.w) << 16);
+  packed.z = (uint32_t)f32_to_bf16(acc1.x) | ((uint32_t)f32_to_bf16(acc1.y) << 16);
+  packed.w = (uint32_t)f32_to_bf16(acc1.z) | ((uint32_t)f32_to_bf16(acc1.w) << 16);
+  reinterpret_cast<uint4*>(out + ((int64_t)b * rows + r) * kDv)[lane] = packed;
+  if (lse_out && lane == 0) lse_out[(int64_t)b * rows + r] = LSE;
+}
+
+}  // namespace mla
+
+extern "C" mla_status mla_merge_states(const float* partial_o, const float* partial_lse,
+                                       const int32_t* split_indptr, int32_t bs,
+                                       int32_t rows_per_req, void* out, float* lse,
+                                       hipStream_t stream) {
+  using namespace mla;
+  if (!partial_o || !partial_lse || !split_indptr || !out)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "mla_merge_states: null pointer");
+  if (bs <= 0) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_merge_states: bs must be positive");
+  if (rows_per_req < 1 || rows_per_req > MLA_MAX_ROWS_PER_REQ)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_merge_states: rows_per_req must be in 1..512");
+  const int64_t waves = (int64_t)bs * rows_per_req;
+  const int64_t blocks = (waves + kMergeWaves - 1) / kMergeWaves;
+  if (blocks > 0x7fffffff) return fail(MLA_ERR_UNSUPPORTED, "mla_merge_states: too many rows");
+  hipLaunchKernelGGL(merge_states_kernel, dim3((unsigned)blocks), dim3(64 * kMergeWaves), 0,
+                     stream, partial_o, partial_lse, split_indptr, bs, rows_per_req,
+                     reinterpret_cast<uint16_t*>(out), lse);
+  return check_launch("mla_merge_states");
+}

@@ -1,0 +1,101 @@
+"""The C ABI library loads and exports every declared symbol; argument errors
+come back as status codes before any launch (CPU only, no GPU calls)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_kv_mla_req_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_decode.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.lib()
+    names = _declared()
+    assert "mla_decode" in names and "mla_merge_states" in names
+    assert "mla_build_block_table" in names and "mla_plan_splits" in names
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, f"binding lacks {n}"
+    assert set(_lib.SIGNATURES) == set(names)
+
+
+def test_version_and_status_strings():
+    lib = _lib.lib()
+    assert lib.mla_abi_version() == 1
+    assert lib.mla_status_string(0) == b"ok"
+    assert lib.mla_status_string(2) == b"unsupported"
+    assert lib.mla_max_total_splits(64, 256) == 320
+    assert lib.mla_partial_bytes(64, 128, 256) == 320 * 128 * 513 * 4
+
+
+P = ctypes.c_void_p
+FAKE = P(0x1000)  # never dereferenced: every case below fails argument checks first
+
+
+def _decode(**kw):
+    a = dict(q=FAKE, bs=2, q_len=1, heads=16, kv=FAKE, dtype=0, pages=8, bt=FAKE, bts=3,
+             sl=FAKE, tp=FAKE, parts=4, ip=FAKE, scale=0.07, causal=1, desc=None, po=FAKE,
+             pl=FAKE, slots=6, out=FAKE, lse=None)
+    a.update(kw)
+    return _lib.lib().mla_decode(a["q"], a["bs"], a["q_len"], a["heads"], a["kv"], a["dtype"],
+                                 a["pages"], a["bt"], a["bts"], a["sl"], a["tp"], a["parts"],
+                                 a["ip"], a["scale"], a["causal"], a["desc"], a["po"], a["pl"],
+                                 a["slots"], a["out"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), _lib.MLA_ERR_INVALID_ARGUMENT),
+    (dict(out=None), _lib.MLA_ERR_INVALID_ARGUMENT),
+    (dict(bs=0), _lib.MLA_ERR_INVALID_ARGUMENT),
+    (dict(heads=-1), _lib.MLA_ERR_INVALID_ARGUMENT),
+    (dict(scale=float("nan")), _lib.MLA_ERR_INVALID_ARGUMENT),
+    (dict(scale=float("inf")), _lib.MLA_ERR_INVALID_ARGUMENT),
+    (dict(dtype=7), _lib.MLA_ERR_UNSUPPORTED),
+    (dict(dtype=1), _lib.MLA_ERR_INVALID_ARGUMENT),          # fp8 without descale
+    (dict(heads=513), _lib.MLA_ERR_UNSUPPORTED),              # rows > 512
+    (dict(q_len=5, heads=128), _lib.MLA_ERR_UNSUPPORTED),     # 640 rows
+    (dict(slots=5), _lib.MLA_ERR_CAPACITY),                   # < bs + parts
+    (dict(parts=513, slots=600), _lib.MLA_ERR_CAPACITY),
+])
+def test_decode_argument_errors(kw, status):
+    assert _decode(**kw) == status
+    assert _lib.lib().mla_last_error_message().startswith(b"mla_decode")
+
+
+def test_block_table_argument_errors():
+    lib = _lib.lib()
+    f = lib.mla_build_block_table
+    assert f(None, 4, 256, FAKE, FAKE, 2, 64, FAKE, 3, -1, -1, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert f(FAKE, 4, 256, FAKE, FAKE, 0, 64, FAKE, 3, -1, -1, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert f(FAKE, 4, 256, FAKE, FAKE, 2, 32, FAKE, 3, -1, -1, None) == _lib.MLA_ERR_UNSUPPORTED
+    # hint needs 4 pages, table has 3
+    assert f(FAKE, 4, 256, FAKE, FAKE, 2, 64, FAKE, 3, -1, 200, None) == _lib.MLA_ERR_CAPACITY
+    # hint needs a slot past the end of req_to_token rows
+    assert f(FAKE, 4, 128, FAKE, FAKE, 2, 64, FAKE, 8, -1, 200, None) == _lib.MLA_ERR_CAPACITY
+
+
+def test_plan_and_merge_argument_errors():
+    lib = _lib.lib()
+    g = lib.mla_plan_splits
+    assert g(None, 2, 16, 4, 0, FAKE, FAKE, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert g(FAKE, 2, 16, 0, 0, FAKE, FAKE, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert g(FAKE, 2, 16, 4, 3, FAKE, FAKE, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert g(FAKE, 2, 0, 4, 0, FAKE, FAKE, None) == _lib.MLA_ERR_UNSUPPORTED
+    assert g(FAKE, 2, 600, 4, 0, FAKE, FAKE, None) == _lib.MLA_ERR_UNSUPPORTED
+    assert g(FAKE, 20000, 16, 4, 0, FAKE, FAKE, None) == _lib.MLA_ERR_CAPACITY
+    assert g(FAKE, 2, 16, 600, 0, FAKE, FAKE, None) == _lib.MLA_ERR_CAPACITY
+    m = lib.mla_merge_states
+    assert m(None, FAKE, FAKE, 2, 16, FAKE, None, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert m(FAKE, FAKE, FAKE, 0, 16, FAKE, None, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert m(FAKE, FAKE, FAKE, 2, 513, FAKE, None, None) == _lib.MLA_ERR_UNSUPPORTED

@@ -135,6 +135,7 @@ def make_custom(
     softmax_scale: float = SOFTMAX_SCALE,
     causal: bool = True,
     ctx_slack: int = 64,
+    with_values: bool = True,
 ) -> Workload:
     """Build a workload with explicit lengths.
 
@@ -143,7 +144,9 @@ def make_custom(
     the batch uses a seeded choice of bs distinct rows.  Slots are
     page-aligned: token j of request b lives at slot 64*page_b[j // 64] + j % 64.
     Cells that the batch does not use hold random valid slots, so a reader
-    that strays gets wrong values rather than a bad address.
+    that strays gets wrong values rather than a bad address.  With
+    ``with_values=False`` only the index data is made (the pool is a single
+    zero page), for tests that never read latent values.
     """
     if kv_dtype not in ("bf16", "fp8_e4m3"):
         raise ValueError(kv_dtype)
@@ -182,6 +185,12 @@ def make_custom(
         q *= np.float32(value_scale)
     q_bits = _bf16_bits(q)
 
+    if not with_values:
+        kv = np.zeros((1, PAGE_SIZE, LATENT_DIM), dtype=np.uint16 if kv_dtype == "bf16" else np.uint8)
+        return Workload(
+            name=name, bs=bs, heads=heads, q_len=q_len, kv_dtype=kv_dtype, q_bits=q_bits, kv=kv,
+            kv_descale=1.0, req_to_token=r2t, req_pool_indices=rpi, seq_lens=seq_lens,
+            softmax_scale=float(np.float32(softmax_scale)), causal=causal, pages=pages)
     x = _normal_pool(rng, pool_pages, value_scale)
     if kv_dtype == "bf16":
         kv = _bf16_bits(x)
