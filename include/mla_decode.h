@@ -179,7 +179,7 @@ int32_t mla_device_num_cus(void);
  * then reads page 0 instead, so it never leaves the pool.
  *
  * Errors: INVALID_ARGUMENT for null pointers, non-positive sizes, a
- * non-finite scale, or fp8 with a NULL kv_descale; UNSUPPORTED for
+ * negative or non-finite scale, or fp8 with a NULL kv_descale; UNSUPPORTED for
  * q_len*num_heads outside 1..512 or an unknown kv_dtype; CAPACITY when
  * partial_slots < bs + num_parts.
  */

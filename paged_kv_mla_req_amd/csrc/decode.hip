@@ -52,6 +52,7 @@ typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 32;
@@ -65,17 +66,10 @@ constexpr int kKSteps = kD / 16;                         // 36 MFMA k-steps for 
 constexpr int kVTiles = kDv / 32;                        // 16 output tiles of 32 columns
 constexpr float kTau = 8.0f;                             // lazy-rescale threshold (log2 units)
 
+// Scalar arguments of the decode kernel (pointers are kernel arguments of
+// their own, marked __restrict__, so the compiler may read the small index
+// arrays through the scalar cache).
 struct DecodeParams {
-  const uint16_t* q;          // bf16 [bs, R, 576]
-  const uint8_t* kv;          // [num_pages, 64, 576] bf16
-  const int32_t* block_table;
-  const int32_t* seq_lens;
-  const int32_t* tile_plan;
-  const int32_t* split_indptr;
-  float* partial_o;           // [slots, R, 512]
-  float* partial_lse;         // [slots, R]
-  uint16_t* out;              // bf16 [bs, R, 512]
-  float* lse;                 // [bs, R] or null
   int64_t num_pages;
   int32_t partial_slots;      // capacity of partial_o / partial_lse
   int32_t bt_stride;
@@ -201,8 +195,272 @@ __device__ __forceinline__ void scale_tile(f32x16& acc, float alpha) {
   for (int i = 0; i < 16; ++i) acc[i] = e[i];
 }
 
+// ---------------------------------------------------------------------------
+// The two MFMA chains of a page are issued from inline assembly in blocks of
+// four MFMAs.  Each block first issues the LDS reads of the *next* block's
+// operands, then its own MFMAs, then waits for those reads: the reads are
+// always in flight behind 128 cycles of matrix work, and no register leaves
+// a block with a load still pending, so the compiler may move or copy any
+// block output freely.  (Left to itself the compiler sinks every read next
+// to its MFMA, because the kernel sits at the 512-register limit.)
+// Hazards the compiler cannot see are covered by hand: 2 wait states before
+// the MFMAs of a block (a VALU write of an operand just before), and 24
+// after the last MFMA of a chain (MFMA result -> VALU / accumulator read;
+// more than the 18 a 16-pass MFMA needs).
+// ---------------------------------------------------------------------------
+
+// S^T block: reads K operands at a[i] + OFF into nk, then 4 MFMAs on k.
+template <int OFF>
+__device__ __forceinline__ void s_block(f32x16& sc, bf16x8 (&nk)[4], const bf16x8 (&k)[4],
+                                        const bf16x8* q, const uint32_t (&a)[4]) {
+  asm volatile(
+      "ds_read_b128 %1, %13 offset:%17\n\t"
+      "ds_read_b128 %2, %14 offset:%17\n\t"
+      "ds_read_b128 %3, %15 offset:%17\n\t"
+      "ds_read_b128 %4, %16 offset:%17\n\t"
+      "s_nop 1\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %5, %9, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %6, %10, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %7, %11, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %8, %12, %0\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "+v"(sc), "=&v"(nk[0]), "=&v"(nk[1]), "=&v"(nk[2]), "=&v"(nk[3])
+      : "v"(k[0]), "v"(k[1]), "v"(k[2]), "v"(k[3]), "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]),
+        "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF));
+}
+
+// First S^T block of a tile: the accumulator starts from 0.
+template <int OFF>
+__device__ __forceinline__ void s_block_first(f32x16& sc, bf16x8 (&nk)[4], const bf16x8 (&k)[4],
+                                              const bf16x8* q, const uint32_t (&a)[4]) {
+  asm volatile(
+      "ds_read_b128 %1, %13 offset:%17\n\t"
+      "ds_read_b128 %2, %14 offset:%17\n\t"
+      "ds_read_b128 %3, %15 offset:%17\n\t"
+      "ds_read_b128 %4, %16 offset:%17\n\t"
+      "s_nop 1\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %5, %9, 0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %6, %10, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %7, %11, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %8, %12, %0\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(sc), "=&v"(nk[0]), "=&v"(nk[1]), "=&v"(nk[2]), "=&v"(nk[3])
+      : "v"(k[0]), "v"(k[1]), "v"(k[2]), "v"(k[3]), "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]),
+        "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF));
+}
+
+// Last S^T block: no further reads; the result is read by VALU next.
+__device__ __forceinline__ void s_block_last(f32x16& sc, const bf16x8 (&k)[4], const bf16x8* q) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %1, %5, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %2, %6, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %3, %7, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %4, %8, %0\n\t"
+      "s_nop 7\n\t"
+      "s_nop 7\n\t"
+      "s_nop 7"
+      : "+v"(sc)
+      : "v"(k[0]), "v"(k[1]), "v"(k[2]), "v"(k[3]), "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]));
+}
+
+// a[i] for column blocks >= 8: the DS offset field stops at 65535.
+template <int G, int TB>
+__device__ __forceinline__ void s_step(f32x16& sc, bf16x8 (&kk)[2][4], const bf16x8 (&qreg)[kKSteps],
+                                       const uint32_t (&a)[4], const uint32_t (&a_hi)[4]) {
+  constexpr int NOFF = 8192 * (G + 1) + TB;  // byte offset of the next group's reads
+  if constexpr (G == 0)
+    s_block_first<NOFF>(sc, kk[1], kk[0], &qreg[0], a);
+  else if constexpr (G + 1 < kKSteps / 4) {
+    if constexpr (NOFF < 65536)
+      s_block<NOFF>(sc, kk[(G + 1) & 1], kk[G & 1], &qreg[4 * G], a);
+    else
+      s_block<NOFF - 32768>(sc, kk[(G + 1) & 1], kk[G & 1], &qreg[4 * G], a_hi);
+  } else {
+    s_block_last(sc, kk[G & 1], &qreg[4 * G]);
+  }
+}
+
+template <int TB, int... G>
+__device__ __forceinline__ void s_chain(f32x16& sc, bf16x8 (&kk)[2][4],
+                                        const bf16x8 (&qreg)[kKSteps], const uint32_t (&a)[4],
+                                        const uint32_t (&a_hi)[4], std::integer_sequence<int, G...>) {
+  (s_step<G, TB>(sc, kk, qreg, a, a_hi), ...);
+}
+
+// S^T for the 32-key tile at byte offset TB of the page: 36 MFMAs.
+// a[i] = page + koff[i] (LDS byte addresses), a_hi[i] = a[i] + 32768.
+template <int TB>
+__device__ __forceinline__ void score_tile(f32x16& sc, const uint32_t (&a)[4],
+                                           const uint32_t (&a_hi)[4],
+                                           const bf16x8 (&qreg)[kKSteps]) {
+  bf16x8 kk[2][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    kk[0][i] = *LDS_PTR(const bf16x8, (uintptr_t)(a[i] + TB));
+  s_chain<TB>(sc, kk, qreg, a, a_hi, std::make_integer_sequence<int, kKSteps / 4>{});
+}
+
+// PV blocks run four MFMAs each (one accumulator tile per MFMA) from a ring
+// of three operand sets: block b computes with set b % 3 and issues the reads
+// of block b + 2 into set (b + 2) % 3, then waits until at most those eight
+// reads are outstanding, i.e. until block b + 1's operands have landed.  The
+// reads of a block therefore have two blocks (256 cycles) of matrix work to
+// arrive.  Set (b + 2) % 3 is an output of block b but is first read by
+// block b + 2, after block b + 1 has waited for it.
+// V^T operand reads of one MFMA: two transposing 8-byte reads (keys
+// kb..kb+3 and kb+4..kb+7) at va[0][par] + off and va[1][par] + off.
+#define MLA_PV_READS                                   \
+  "ds_read_b64_tr_b16 %4, %17 offset:%21\n\t"          \
+  "ds_read_b64_tr_b16 %8, %18 offset:%21\n\t"          \
+  "ds_read_b64_tr_b16 %5, %19 offset:%21\n\t"          \
+  "ds_read_b64_tr_b16 %9, %20 offset:%21\n\t"          \
+  "ds_read_b64_tr_b16 %6, %17 offset:%22\n\t"          \
+  "ds_read_b64_tr_b16 %10, %18 offset:%22\n\t"         \
+  "ds_read_b64_tr_b16 %7, %19 offset:%22\n\t"          \
+  "ds_read_b64_tr_b16 %11, %20 offset:%22\n\t"
+
+// Block with reads ahead.  WAIT is the number of LDS reads allowed to stay
+// outstanding at the end (8: the ones just issued).
+template <int OFF0, int OFF1, int WAIT>
+__device__ __forceinline__ void pv_block_rd(f32x16& o0, f32x16& o1, f32x16& o2, f32x16& o3,
+                                            bf16x4 (&nlo)[4], bf16x4 (&nhi)[4],
+                                            const bf16x8 (&v)[4], bf16x8 p,
+                                            const uint32_t (&va)[2][2]) {
+  asm volatile(
+      MLA_PV_READS
+      "s_nop 1\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %12, %16, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %1, %13, %16, %1\n\t"
+      "v_mfma_f32_32x32x16_bf16 %2, %14, %16, %2\n\t"
+      "v_mfma_f32_32x32x16_bf16 %3, %15, %16, %3\n\t"
+      "s_waitcnt lgkmcnt(%23)"
+      : "+a"(o0), "+a"(o1), "+a"(o2), "+a"(o3), "=&v"(nlo[0]), "=&v"(nlo[1]), "=&v"(nlo[2]),
+        "=&v"(nlo[3]), "=&v"(nhi[0]), "=&v"(nhi[1]), "=&v"(nhi[2]), "=&v"(nhi[3])
+      : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(p), "v"(va[0][0]), "v"(va[1][0]),
+        "v"(va[0][1]), "v"(va[1][1]), "i"(OFF0), "i"(OFF1), "i"(WAIT));
+}
+
+// Block without reads; WAIT as above (0: drain), LAST adds the tail that
+// lets VALU read the accumulators next.
+template <int WAIT, bool LAST>
+__device__ __forceinline__ void pv_block_nord(f32x16& o0, f32x16& o1, f32x16& o2, f32x16& o3,
+                                              const bf16x8 (&v)[4], bf16x8 p) {
+  if constexpr (LAST)
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_mfma_f32_32x32x16_bf16 %0, %4, %8, %0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %1, %5, %8, %1\n\t"
+        "v_mfma_f32_32x32x16_bf16 %2, %6, %8, %2\n\t"
+        "v_mfma_f32_32x32x16_bf16 %3, %7, %8, %3\n\t"
+        "s_nop 7\n\t"
+        "s_nop 7\n\t"
+        "s_nop 7"
+        : "+a"(o0), "+a"(o1), "+a"(o2), "+a"(o3)
+        : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(p));
+  else
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_mfma_f32_32x32x16_bf16 %0, %4, %8, %0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %1, %5, %8, %1\n\t"
+        "v_mfma_f32_32x32x16_bf16 %2, %6, %8, %2\n\t"
+        "v_mfma_f32_32x32x16_bf16 %3, %7, %8, %3\n\t"
+        "s_waitcnt lgkmcnt(%9)"
+        : "+a"(o0), "+a"(o1), "+a"(o2), "+a"(o3)
+        : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(p), "i"(WAIT));
+}
+
+constexpr int kPvBlocks = 2 * kVTiles / 4;  // 8 blocks of 4 MFMAs per 32-key tile
+
+// LDS offsets (relative to va) of block nb's reads: MFMA i = 4 nb + j has
+// u = i / 16 (keys 8u..8u+7 of the lane half) and vt = i % 16; MFMAs j = 0, 1
+// share column block vt/2 (OFF0), j = 2, 3 the next one (OFF1).
+template <int T, int NB>
+struct PvOff {
+  static constexpr int n0 = 4 * NB, nu = n0 / kVTiles, nvt = n0 % kVTiles;
+  static constexpr int row = (32 * T + 8 * nu) * 128;
+  static constexpr int off0 = row + 8192 * (nvt >> 1);
+  static constexpr int off1 = row + 8192 * ((nvt + 2) >> 1);
+};
+
+template <int T, int B>
+__device__ __forceinline__ void pv_step(f32x16 (&oacc)[kVTiles], bf16x8 (&ring)[3][4],
+                                        const bf16x8 (&pop)[2], const uint32_t (&va)[2][2]) {
+  constexpr int u = (4 * B) / kVTiles, vt0 = (4 * B) % kVTiles;
+  bf16x8(&cur)[4] = ring[B % 3];
+  if constexpr (B + 2 < kPvBlocks) {
+    bf16x4 nlo[4], nhi[4];
+    pv_block_rd<PvOff<T, B + 2>::off0, PvOff<T, B + 2>::off1, 8>(
+        oacc[vt0], oacc[vt0 + 1], oacc[vt0 + 2], oacc[vt0 + 3], nlo, nhi, cur, pop[u], va);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      ring[(B + 2) % 3][j] = __builtin_shufflevector(nlo[j], nhi[j], 0, 1, 2, 3, 4, 5, 6, 7);
+  } else if constexpr (B + 1 < kPvBlocks) {
+    pv_block_nord<0, false>(oacc[vt0], oacc[vt0 + 1], oacc[vt0 + 2], oacc[vt0 + 3], cur, pop[u]);
+  } else {
+    pv_block_nord<0, true>(oacc[vt0], oacc[vt0 + 1], oacc[vt0 + 2], oacc[vt0 + 3], cur, pop[u]);
+  }
+}
+
+template <int T, int... B>
+__device__ __forceinline__ void pv_chain(f32x16 (&oacc)[kVTiles], bf16x8 (&ring)[3][4],
+                                         const bf16x8 (&pop)[2], const uint32_t (&va)[2][2],
+                                         std::integer_sequence<int, B...>) {
+  (pv_step<T, B>(oacc, ring, pop, va), ...);
+}
+
+// Reads of blocks 0 and 1 for tile T; returns with block 0's operands landed
+// and block 1's eight reads possibly outstanding.
+template <int T>
+__device__ __forceinline__ void pv_prologue(bf16x8 (&ring)[3][4], const uint32_t (&va)[2][2]) {
+  bf16x4 lo0[4], hi0[4], lo1[4], hi1[4];
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16 offset:%20\n\t"
+      "ds_read_b64_tr_b16 %4, %17 offset:%20\n\t"
+      "ds_read_b64_tr_b16 %1, %18 offset:%20\n\t"
+      "ds_read_b64_tr_b16 %5, %19 offset:%20\n\t"
+      "ds_read_b64_tr_b16 %2, %16 offset:%21\n\t"
+      "ds_read_b64_tr_b16 %6, %17 offset:%21\n\t"
+      "ds_read_b64_tr_b16 %3, %18 offset:%21\n\t"
+      "ds_read_b64_tr_b16 %7, %19 offset:%21\n\t"
+      "ds_read_b64_tr_b16 %8, %16 offset:%22\n\t"
+      "ds_read_b64_tr_b16 %12, %17 offset:%22\n\t"
+      "ds_read_b64_tr_b16 %9, %18 offset:%22\n\t"
+      "ds_read_b64_tr_b16 %13, %19 offset:%22\n\t"
+      "ds_read_b64_tr_b16 %10, %16 offset:%23\n\t"
+      "ds_read_b64_tr_b16 %14, %17 offset:%23\n\t"
+      "ds_read_b64_tr_b16 %11, %18 offset:%23\n\t"
+      "ds_read_b64_tr_b16 %15, %19 offset:%23\n\t"
+      "s_waitcnt lgkmcnt(8)"
+      : "=&v"(lo0[0]), "=&v"(lo0[1]), "=&v"(lo0[2]), "=&v"(lo0[3]), "=&v"(hi0[0]), "=&v"(hi0[1]),
+        "=&v"(hi0[2]), "=&v"(hi0[3]), "=&v"(lo1[0]), "=&v"(lo1[1]), "=&v"(lo1[2]),
+        "=&v"(lo1[3]), "=&v"(hi1[0]), "=&v"(hi1[1]), "=&v"(hi1[2]), "=&v"(hi1[3])
+      : "v"(va[0][0]), "v"(va[1][0]), "v"(va[0][1]), "v"(va[1][1]), "i"(PvOff<T, 0>::off0),
+        "i"(PvOff<T, 0>::off1), "i"(PvOff<T, 1>::off0), "i"(PvOff<T, 1>::off1));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    ring[0][j] = __builtin_shufflevector(lo0[j], hi0[j], 0, 1, 2, 3, 4, 5, 6, 7);
+    ring[1][j] = __builtin_shufflevector(lo1[j], hi1[j], 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+}
+
+// O^T += V^T P^T for 32-key tile T: 32 MFMAs.  va[e][par] = page + voff.
+template <int T>
+__device__ __forceinline__ void pv_tile(f32x16 (&oacc)[kVTiles], const bf16x8 (&pop)[2],
+                                        const uint32_t (&va)[2][2]) {
+  bf16x8 ring[3][4];
+  pv_prologue<T>(ring, va);
+  pv_chain<T>(oacc, ring, pop, va, std::make_integer_sequence<int, kPvBlocks>{});
+}
+
 __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
-mla_decode_bf16_kernel(DecodeParams P) {
+mla_decode_bf16_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
+                       const int32_t* __restrict__ block_table,
+                       const int32_t* __restrict__ seq_lens,
+                       const int32_t* __restrict__ tile_plan,
+                       const int32_t* __restrict__ split_indptr, float* __restrict__ partial_o,
+                       float* __restrict__ partial_lse, uint16_t* __restrict__ out,
+                       float* __restrict__ lse_out, DecodeParams P) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kPageBytes];
 
   const int lane = threadIdx.x & 63;
@@ -211,7 +469,7 @@ mla_decode_bf16_kernel(DecodeParams P) {
   const int h = lane >> 5;      // lane half
   const int part = blockIdx.x;
 
-  const int32_t* tp = P.tile_plan + part * 8;
+  const int32_t* tp = tile_plan + part * 8;
   const int b_first = tp[0], pg_first = tp[1], b_last = tp[2], pg_last = tp[3];
   const int first_piece = tp[4], total = tp[5];
   // An empty part, or a row no planner would produce, does nothing (the
@@ -225,26 +483,26 @@ mla_decode_bf16_kernel(DecodeParams P) {
   const bool wave_active = row0 < P.rows;
   const bool row_valid = r < P.rows;
   const int i_tok = row_valid ? r / P.heads : 0;
+  const int i_tok_min = row0 / P.heads;  // smallest token index among the wave's rows
 
   // ---- per-lane LDS offsets (relative to a page buffer) -------------------
   // Page loads: key i/8 of the group, chunk slot i%8 <- source chunk
   // (i%8) ^ (4 bit4(i) + 2 bit5(i) + bit1(wave)).
   const uint32_t load_voff0 =
-      (wave + 0) * (8 * kRowBytes) + (lane >> 3) * kRowBytes +
+      wave * (8 * kRowBytes) + (lane >> 3) * kRowBytes +
       16 * ((lane & 7) ^ (4 * ((lane >> 4) & 1) + 2 * ((lane >> 5) & 1) + ((wave >> 1) & 1)));
   const uint32_t load_voff1 = load_voff0 + 4 * (8 * kRowBytes);  // key group wave + 4
   // S^T A operand: lane (m = n, h) reads key 32t + sigma(m) with
   // sigma(8q + 4g + t') = 16g + 4q + t', global chunk 2ks + h, i.e. column
-  // block ks/4, chunk 2(ks%4) + h of the block.
+  // block ks/4, chunk 2(ks%4) + h of the block.  Keys 32 apart share the
+  // swizzle, so tile 1 is tile 0 plus 32 rows of 128 bytes.
   const int sig = 16 * ((n >> 2) & 1) + 4 * (n >> 3) + (n & 3);
-  uint32_t koff[2][4];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int key = 32 * t + sig;
-    const int sw = 4 * ((key >> 1) & 1) + 2 * ((key >> 2) & 1) + ((key >> 4) & 1);
+  uint32_t koff[4];
+  {
+    const int sw = 4 * ((sig >> 1) & 1) + 2 * ((sig >> 2) & 1) + ((sig >> 4) & 1);
     const int x = h ^ sw;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) koff[t][i] = key * 128 + (((2 * i) ^ x) << 4);
+    for (int i = 0; i < 4; ++i) koff[i] = sig * 128 + (((2 * i) ^ x) << 4);
   }
   // V^T A operand via ds_read_b64_tr_b16: in the 16-lane block (c16, s16)
   // of half h, source lane s16 addresses key kb + 4e + s16/4 (kb a multiple
@@ -270,32 +528,39 @@ mla_decode_bf16_kernel(DecodeParams P) {
     reinterpret_cast<u32x4*>(smem)[i] = (u32x4){0, 0, 0, 0};
   __syncthreads();
 
-  // ---- page cursor for prefetch -------------------------------------------
+  // ---- page cursor for prefetch ----------------------------------------------
+  // (nb, np) is the page whose loads are issued next; its block-table entry
+  // and length were read one page earlier so the scalar loads never stall.
   int nb = b_first, np = pg_first;
-  int nlen = P.seq_lens[nb];
+  int nlen = seq_lens[nb];
   int nend = (nb == b_last) ? pg_last : page_count(nlen);
   auto phys_of = [&](int b, int p) -> int64_t {
     if (p >= P.bt_stride) return 0;
-    int64_t pg = P.block_table[(int64_t)b * P.bt_stride + p];
+    const int64_t pg = block_table[(int64_t)b * P.bt_stride + p];
     return (pg >= 0 && pg < P.num_pages) ? pg : 0;
   };
+  int64_t nphys = phys_of(nb, np);
+  int nrows = min(kPage, max(0, nlen - np * kPage));
+  auto issue = [&](uint8_t* buf) {
+    issue_page_loads(page_rsrc(kv + nphys * kPageBytes, __builtin_amdgcn_readfirstlane(nrows)),
+                     buf, wave, load_voff0, load_voff1);
+  };
+  // Move the cursor one page on and read that page's block-table entry and
+  // length.  Called after a page's compute, so the scalar loads have a whole
+  // barrier interval to land before the next issue needs them.
   auto advance = [&]() {
     ++np;
     while (np >= nend && nb < b_last) {
       ++nb;
       np = 0;
-      nlen = P.seq_lens[nb];
+      nlen = seq_lens[nb];
       nend = (nb == b_last) ? pg_last : page_count(nlen);
     }
-  };
-  // loads of the page under the prefetch cursor: only its rows below the length
-  auto issue_next = [&](uint8_t* buf) {
-    const int rows = __builtin_amdgcn_readfirstlane(min(kPage, max(0, nlen - np * kPage)));
-    issue_page_loads(page_rsrc(P.kv + phys_of(nb, np) * kPageBytes, rows), buf, wave,
-                     load_voff0, load_voff1);
+    nphys = phys_of(nb, np);
+    nrows = min(kPage, max(0, nlen - np * kPage));
   };
 
-  issue_next(smem);
+  issue(smem);
   advance();
 
   // Every wave passes exactly `total` barriers, one per page, whatever the
@@ -307,7 +572,7 @@ mla_decode_bf16_kernel(DecodeParams P) {
       __builtin_amdgcn_s_waitcnt(0x0f70);
       __syncthreads();
       if (it + 1 < total) {
-        issue_next(smem + ((it + 1) & 1) * kPageBytes);
+        issue(smem + ((it + 1) & 1) * kPageBytes);
         advance();
       }
     }
@@ -322,11 +587,14 @@ mla_decode_bf16_kernel(DecodeParams P) {
   int piece = first_piece;
   while (true) {
     // ---- one piece: pages [cp, cend) of request cb ---------------------------
-    const int cend = (cb == b_last) ? pg_last : page_count(P.seq_lens[cb]);
-    const int32_t L = P.seq_lens[cb];
+    const int32_t L = seq_lens[cb];
+    const int cend = (cb == b_last) ? pg_last : page_count(L);
     const int32_t lim = P.causal ? L - P.q_len + i_tok : L - 1;  // last visible key
+    // pages from first_masked on may hold keys some row of this wave cannot see
+    const int32_t lim_min = P.causal ? L - P.q_len + i_tok_min : L - 1;
+    const int first_masked = lim_min >= 0 ? (lim_min + 1) / kPage : 0;
     {
-      const uint16_t* qrow = P.q + ((int64_t)cb * P.rows + (row_valid ? r : 0)) * kD + 8 * h;
+      const uint16_t* qrow = q + ((int64_t)cb * P.rows + (row_valid ? r : 0)) * kD + 8 * h;
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
         u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 16 * ks);
@@ -336,105 +604,103 @@ mla_decode_bf16_kernel(DecodeParams P) {
     }
 #pragma unroll
     for (int vt = 0; vt < kVTiles; ++vt) oacc[vt] = (f32x16){};
-    float m_run = -INFINITY, l_run = 0.f, lr_run = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
 
     for (; cp < cend && it < total; ++cp, ++it) {
       __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of page `it` landed
       __syncthreads();                     // ... and every wave's; buffer it+1 is free again
-      uint8_t* cur = smem + (it & 1) * kPageBytes;
-      if (it + 1 < total) {
-        issue_next(smem + ((it + 1) & 1) * kPageBytes);
-        advance();
-      }
+      const lds_u8* base = LDS_PTR(uint8_t, smem) + (it & 1) * kPageBytes;
+      if (it + 1 < total) issue(smem + ((it + 1) & 1) * kPageBytes);
 
-      const uint32_t base = (uint32_t)(uintptr_t)LDS_PTR(uint8_t, cur);
+      // LDS byte addresses of this page's operands
+      const uint32_t pbase = (uint32_t)(uintptr_t)base;
+      uint32_t ka[4], ka_hi[4], va[2][2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ka[i] = pbase + koff[i];
+        ka_hi[i] = ka[i] + 32768;
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int par = 0; par < 2; ++par) va[e][par] = pbase + voff[e][par];
+
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        // ---- S^T = K Q^T for 32-key tile t ---------------------------------------
-        f32x16 sc = {};
-#pragma unroll
-        for (int g = 0; g < kKSteps / 4; ++g) {
-          // k-steps 4g .. 4g+3 = column block g, chunks 2i + h
-          const uint32_t a = base + 8192 * g;
-          bf16x8 k0 = *LDS_PTR(bf16x8, (uintptr_t)(a + koff[t][0]));
-          bf16x8 k1 = *LDS_PTR(bf16x8, (uintptr_t)(a + koff[t][1]));
-          bf16x8 k2 = *LDS_PTR(bf16x8, (uintptr_t)(a + koff[t][2]));
-          bf16x8 k3 = *LDS_PTR(bf16x8, (uintptr_t)(a + koff[t][3]));
-          if (g + 1 < kKSteps / 4)
-            mfma_s4(sc, k0, k1, k2, k3, qreg[4 * g], qreg[4 * g + 1], qreg[4 * g + 2],
-                    qreg[4 * g + 3]);
-          else
-            mfma_s4_last(sc, k0, k1, k2, k3, qreg[4 * g], qreg[4 * g + 1], qreg[4 * g + 2],
-                         qreg[4 * g + 3]);
-        }
-        // ---- mask, scale, running max ----------------------------------------------
-        // sc[i] belongs to key 32t + 16h + i of this page.
+        // ---- S^T = K Q^T for 32-key tile t; sc[i] is key 32t + 16h + i -----------
+        f32x16 sc;
+        if (t == 0)
+          score_tile<0>(sc, ka, ka_hi, qreg);
+        else
+          score_tile<32 * 128>(sc, ka, ka_hi, qreg);
+        // ---- row max of the scaled scores; weights p = 2^(c s - m) -----------------
+        // c = softmax_scale * log2(e) > 0, so max(c s) = c max(s).  Keys a row
+        // cannot see (causal limit, page tail) are excluded on the pages
+        // where they can occur.
         const int key0 = cp * kPage + 32 * t + 16 * h;
+        const bool masked = cp >= first_masked;
         float mloc = -INFINITY;
+        if (masked) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float v = sc[i] * P.scale_log2;
-          v = (key0 + i <= lim) ? v : -INFINITY;
-          sc[i] = v;
-          mloc = fmaxf(mloc, v);
+          for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, (key0 + i <= lim) ? sc[i] : -INFINITY);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; i += 2) mloc = fmaxf(mloc, fmaxf(sc[i], sc[i + 1]));
         }
         mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-        const bool need = mloc > m_run + kTau;
+        const float m_tile = (mloc == -INFINITY) ? -INFINITY : P.scale_log2 * mloc;
+        const bool need = m_tile > m_run + kTau;
         if (__any(need)) {
-          const float m_new = need ? mloc : m_run;
+          const float m_new = need ? m_tile : m_run;
           const float alpha = need ? exp2f(m_run - m_new) : 1.0f;
           l_run *= alpha;
-          lr_run *= alpha;
+          // Rows whose running max is still -inf have o = 0: only a wave with
+          // some earlier weight needs the 256-register rescale.
+          if (__any(need && m_run != -INFINITY)) {
 #pragma unroll
-          for (int vt = 0; vt < kVTiles; ++vt) scale_tile(oacc[vt], alpha);
+            for (int vt = 0; vt < kVTiles; ++vt) scale_tile(oacc[vt], alpha);
+          }
           m_run = m_new;
         }
-        const float mref = (m_run == -INFINITY) ? 0.f : m_run;
-        // ---- P = 2^(s - m), row sum, bf16 B operand ---------------------------------
-        // Two row sums: of the exact weights (for lse) and of the bf16-rounded
-        // weights the MFMA uses (to normalise o, which then stays an exact
-        // convex combination of the value rows).
+        const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
         bf16x8 pop[2];
+        if (masked) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = exp2f(sc[i] - mref);
-          const __bf16 pb = (__bf16)p;
-          l_run += p;
-          lr_run += (float)pb;
-          pop[i >> 3][i & 7] = pb;
-        }
-        // ---- O^T += V^T P^T -------------------------------------------------------------
-        // MFMA u covers keys 32t + 16h + 8u + 0..7 in lane half h.
+          for (int i = 0; i < 16; ++i) {
+            const float e = __builtin_amdgcn_exp2f(fmaf(sc[i], P.scale_log2, neg_m));
+            const float p = (key0 + i <= lim) ? e : 0.f;
+            l_run += p;
+            pop[i >> 3][i & 7] = (__bf16)p;
+          }
+        } else {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const uint32_t ub = base + (32 * t + 8 * u) * 128;
-#pragma unroll
-          for (int vt = 0; vt < kVTiles; ++vt) {
-            const uint32_t col = 8192 * (vt >> 1);
-            bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                LDS_PTR(bf16x4, (uintptr_t)(ub + voff[0][vt & 1] + col)));
-            bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                LDS_PTR(bf16x4, (uintptr_t)(ub + voff[1][vt & 1] + col)));
-            bf16x8 vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            oacc[vt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[u], oacc[vt], 0, 0, 0);
+          for (int i = 0; i < 16; ++i) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(sc[i], P.scale_log2, neg_m));
+            l_run += p;
+            pop[i >> 3][i & 7] = (__bf16)p;
           }
         }
+        // ---- O^T += V^T P^T ------------------------------------------------------------
+        if (t == 0)
+          pv_tile<0>(oacc, pop, va);
+        else
+          pv_tile<1>(oacc, pop, va);
       }
+      if (it + 1 < total) advance();
     }
 
     // ---- epilogue of the piece ---------------------------------------------------
     {
       const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-      const float lr_tot = lr_run + __shfl_xor(lr_run, 32, 64);
-      const float inv = lr_tot > 0.f ? 1.0f / lr_tot : 0.f;
+      const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
       const float lse_val =
           l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
-      const int k0 = P.split_indptr[cb];
-      const int k = P.split_indptr[cb + 1] - k0;
+      const int k0 = split_indptr[cb];
+      const int k = split_indptr[cb + 1] - k0;
       if (row_valid) {
         const int64_t slot = (int64_t)k0 + piece;
         if (k > 1 && slot < P.partial_slots) {
-          float* dst = P.partial_o + (slot * P.rows + r) * kDv + 4 * h;
+          float* dst = partial_o + (slot * P.rows + r) * kDv + 4 * h;
 #pragma unroll
           for (int vt = 0; vt < kVTiles; ++vt)
 #pragma unroll
@@ -443,9 +709,9 @@ mla_decode_bf16_kernel(DecodeParams P) {
                                      oacc[vt][4 * g + 2] * inv, oacc[vt][4 * g + 3] * inv);
               *reinterpret_cast<float4*>(dst + 32 * vt + 8 * g) = v;
             }
-          if (h == 0) P.partial_lse[slot * P.rows + r] = lse_val;
+          if (h == 0) partial_lse[slot * P.rows + r] = lse_val;
         } else if (k <= 1) {
-          uint16_t* dst = P.out + ((int64_t)cb * P.rows + r) * kDv + 4 * h;
+          uint16_t* dst = out + ((int64_t)cb * P.rows + r) * kDv + 4 * h;
 #pragma unroll
           for (int vt = 0; vt < kVTiles; ++vt)
 #pragma unroll
@@ -457,7 +723,7 @@ mla_decode_bf16_kernel(DecodeParams P) {
                     ((uint32_t)f32_to_bf16(oacc[vt][4 * g + 3] * inv) << 16);
               *reinterpret_cast<uint2*>(dst + 32 * vt + 8 * g) = v;
             }
-          if (P.lse && h == 0) P.lse[(int64_t)cb * P.rows + r] = lse_val;
+          if (lse_out && h == 0) lse_out[(int64_t)cb * P.rows + r] = lse_val;
         }
       }
     }
@@ -465,7 +731,7 @@ mla_decode_bf16_kernel(DecodeParams P) {
     // next request of the part that has pages
     do {
       ++cb;
-    } while (cb < b_last && page_count(P.seq_lens[cb]) <= 0);
+    } while (cb < b_last && page_count(seq_lens[cb]) <= 0);
     cp = 0;
     piece = 0;
   }
@@ -493,8 +759,8 @@ extern "C" mla_status mla_decode(const void* q, int32_t bs, int32_t q_len, int32
   if (bs <= 0 || q_len <= 0 || num_heads <= 0 || num_pages <= 0 || bt_row_stride <= 0 ||
       num_parts <= 0)
     return fail(MLA_ERR_INVALID_ARGUMENT, "mla_decode: sizes must be positive");
-  if (!std::isfinite(softmax_scale))
-    return fail(MLA_ERR_INVALID_ARGUMENT, "mla_decode: softmax_scale is not finite");
+  if (!std::isfinite(softmax_scale) || softmax_scale < 0.f)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "mla_decode: softmax_scale must be finite and >= 0");
   if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3)
     return fail(MLA_ERR_UNSUPPORTED, "mla_decode: unknown kv_dtype");
   if (kv_dtype == MLA_KV_FP8_E4M3 && !kv_descale)
@@ -510,16 +776,6 @@ extern "C" mla_status mla_decode(const void* q, int32_t bs, int32_t q_len, int32
     return fail(MLA_ERR_UNSUPPORTED, "mla_decode: fp8 cache not built yet");
 
   DecodeParams p;
-  p.q = reinterpret_cast<const uint16_t*>(q);
-  p.kv = reinterpret_cast<const uint8_t*>(kv_cache);
-  p.block_table = block_table;
-  p.seq_lens = seq_lens;
-  p.tile_plan = tile_plan;
-  p.split_indptr = split_indptr;
-  p.partial_o = partial_o;
-  p.partial_lse = partial_lse;
-  p.out = reinterpret_cast<uint16_t*>(out);
-  p.lse = lse;
   p.num_pages = num_pages;
   p.partial_slots = partial_slots;
   p.bt_stride = bt_row_stride;
@@ -530,6 +786,9 @@ extern "C" mla_status mla_decode(const void* q, int32_t bs, int32_t q_len, int32
   p.causal = causal ? 1 : 0;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   dim3 grid(num_parts, (unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
-  hipLaunchKernelGGL(mla_decode_bf16_kernel, grid, dim3(kWaves * 64), 0, stream, p);
+  hipLaunchKernelGGL(mla_decode_bf16_kernel, grid, dim3(kWaves * 64), 0, stream,
+                     reinterpret_cast<const uint16_t*>(q), reinterpret_cast<const uint8_t*>(kv_cache),
+                     block_table, seq_lens, tile_plan, split_indptr, partial_o, partial_lse,
+                     reinterpret_cast<uint16_t*>(out), lse, p);
   return check_launch("mla_decode");
 }

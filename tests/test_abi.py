@@ -61,6 +61,7 @@ def _decode(**kw):
     (dict(heads=-1), _lib.MLA_ERR_INVALID_ARGUMENT),
     (dict(scale=float("nan")), _lib.MLA_ERR_INVALID_ARGUMENT),
     (dict(scale=float("inf")), _lib.MLA_ERR_INVALID_ARGUMENT),
+    (dict(scale=-0.5), _lib.MLA_ERR_INVALID_ARGUMENT),
     (dict(dtype=7), _lib.MLA_ERR_UNSUPPORTED),
     (dict(dtype=1), _lib.MLA_ERR_INVALID_ARGUMENT),          # fp8 without descale
     (dict(heads=513), _lib.MLA_ERR_UNSUPPORTED),              # rows > 512
