@@ -39,6 +39,11 @@ def _args():
                          "256 MB last-level cache cannot serve a step from the previous one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-runs", type=int, default=3)
+    ap.add_argument("--decode-launches", type=int, default=30,
+                    help="back-to-back decode launches timed for the kernel's launch duration")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one device-to-device copy of this many MiB before warm-up, as the "
+                         "known-size reference kernel for HBM byte counters")
     return ap.parse_args()
 
 
@@ -55,6 +60,24 @@ def _algorithmic_bytes(w) -> dict:
     lse = w.bs * R * 4
     bt = int((-(-L // 64)).sum()) * 4
     return dict(kv=kv, q=q, o=o, lse=lse, bt=bt, total=kv + q + o + lse + bt)
+
+
+def _traffic(root: str, kernel_src: str):
+    """HBM bytes per decode launch from the committed counter summary, or None
+    when that summary is missing or was taken on another version of the
+    kernel source (sha256 recorded in the file)."""
+    import hashlib
+    path = os.path.join(root, "profiles", "mla_decode_bf16_dsv3_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        with open(kernel_src, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(w, runs: int) -> dict:
@@ -127,6 +150,11 @@ def main() -> int:
     max_len = int(w.seq_lens.max())
     ev = []  # (start, end) events around each decode launch of the timed steps
 
+    def decode(p):
+        mla.mla_decode(p.q, p.kv, bt, p.seq_lens, tile_plan, split_indptr, w.softmax_scale,
+                       partial_o=po, partial_lse=pl, out=out, lse=lse, kv_dtype=w.kv_dtype,
+                       kv_descale=p.kv_descale, causal=w.causal)
+
     def step(i: int, record: bool):
         p = pools[i % len(pools)]
         mla.build_block_table(p.req_to_token, p.req_pool_indices, p.seq_lens, width,
@@ -136,14 +164,20 @@ def main() -> int:
         if record:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-        mla.mla_decode(p.q, p.kv, bt, p.seq_lens, tile_plan, split_indptr, w.softmax_scale,
-                       partial_o=po, partial_lse=pl, out=out, lse=lse, kv_dtype=w.kv_dtype,
-                       kv_descale=p.kv_descale, causal=w.causal)
+        decode(p)
         if record:
             e1.record()
             ev.append((e0, e1))
         mla.merge_states(po, pl, split_indptr, out, lse)
 
+    if a.calib_copy_mib > 0:
+        n = a.calib_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)  # the reference kernel for FETCH_SIZE / WRITE_SIZE: n bytes each way
+        torch.cuda.synchronize()
+        del src, dst
     print(f"[bench] warmup {a.warmup} steps", file=sys.stderr, flush=True)
     for i in range(a.warmup):
         step(i, False)
@@ -155,7 +189,20 @@ def main() -> int:
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / a.steps
-    dec_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    dec_in_step_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    # The decode kernel's launch duration: events bracketing back-to-back
+    # launches on the stream the kernel runs on (the plan and block table of
+    # the last step are reused; the pools still rotate, so no launch finds its
+    # KV in the caches).  An event pair around a single launch also counts the
+    # dispatch and end-of-kernel fences, which this amortises away.
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(a.decode_launches):
+        decode(pools[i % len(pools)])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dec_ms = e0.elapsed_time(e1) / a.decode_launches
 
     b = _algorithmic_bytes(w)
     kv_gbs = b["kv"] / (ms_step * 1e-3) / 1e9
@@ -189,13 +236,16 @@ def main() -> int:
         "pct_hbm_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(tokens_s, 1),
         "decode_kernel_ms": round(dec_ms, 5),
+        "decode_in_step_event_ms": round(dec_in_step_ms, 5),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": _traffic(os.path.dirname(os.path.abspath(__file__)),
+                                os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                             "paged_kv_mla_req_amd", "csrc", "decode.hip")),
             "kernel": "mla_decode_bf16_kernel",
             "bytes_per_launch": b["total"],
         },
