@@ -39,11 +39,14 @@ def _args():
                          "256 MB last-level cache cannot serve a step from the previous one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-runs", type=int, default=3)
-    ap.add_argument("--decode-launches", type=int, default=30,
-                    help="back-to-back decode launches timed for the kernel's launch duration")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
-                    help="run one device-to-device copy of this many MiB before warm-up, as the "
-                         "known-size reference kernel for HBM byte counters")
+                    help="before warm-up, run one plain elementwise kernel (bitwise not) that "
+                         "reads and writes this many MiB: the known-size reference for HBM "
+                         "byte counters")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU run: turn two rocprofv3 --pmc counter_collection.csv files "
+                         "(FETCH_SIZE, then WRITE_SIZE, of a run with --calib-copy-mib) into "
+                         "HBM bytes per decode launch and store them under profiles/")
     return ap.parse_args()
 
 
@@ -62,12 +65,18 @@ def _algorithmic_bytes(w) -> dict:
     return dict(kv=kv, q=q, o=o, lse=lse, bt=bt, total=kv + q + o + lse + bt)
 
 
-def _traffic(root: str, kernel_src: str):
+def _traffic_path(root: str, workload: str) -> str:
+    from workloads import CONFIGS
+    tag = "bf16" if CONFIGS[workload]["kv_dtype"] == "bf16" else "fp8"
+    return os.path.join(root, "profiles", f"mla_decode_{tag}_{workload}_traffic.json")
+
+
+def _traffic(root: str, kernel_src: str, workload: str):
     """HBM bytes per decode launch from the committed counter summary, or None
     when that summary is missing or was taken on another version of the
     kernel source (sha256 recorded in the file)."""
     import hashlib
-    path = os.path.join(root, "profiles", "mla_decode_bf16_dsv3_traffic.json")
+    path = _traffic_path(root, workload)
     try:
         with open(path) as f:
             rec = json.load(f)
@@ -78,6 +87,41 @@ def _traffic(root: str, kernel_src: str):
     if rec.get("kernel_source_sha256") != sha:
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def traffic_from_counters(fetch_csv: str, write_csv: str, calib_mib: int, root: str) -> dict:
+    """HBM bytes per decode launch from FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled by calib_mib MiB over what the same counter read
+    for the calibration kernel (bitwise not over calib_mib MiB)."""
+    import csv
+    import hashlib
+
+    def read(path, counter):
+        dec, cal = [], []
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                v = float(r["Counter_Value"]) * 1024.0
+                if "mla_decode_kernel" in r["Kernel_Name"]:
+                    dec.append(v)
+                elif "bitwise_not" in r["Kernel_Name"].lower():
+                    cal.append(v)
+        if not dec or not cal:
+            raise SystemExit(f"{path}: no decode or calibration dispatches for {counter}")
+        factor = calib_mib * 2.0**20 / max(cal)
+        return float(np.mean(dec)) * factor, factor, float(np.mean(dec))
+
+    fetch, f_fac, f_raw = read(fetch_csv, "FETCH_SIZE")
+    write, w_fac, w_raw = read(write_csv, "WRITE_SIZE")
+    src = os.path.join(root, "paged_kv_mla_req_amd", "csrc", "decode.hip")
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    return {"hbm_bytes_per_launch": round(fetch + write), "fetch_bytes": round(fetch),
+            "write_bytes": round(write), "fetch_raw_bytes": round(f_raw),
+            "write_raw_bytes": round(w_raw), "fetch_scale": round(f_fac, 4),
+            "write_scale": round(w_fac, 4), "calibration_mib": calib_mib,
+            "kernel_source_sha256": sha}
 
 
 def cpu_baseline(w, runs: int) -> dict:
@@ -117,6 +161,16 @@ def cpu_baseline(w, runs: int) -> dict:
 
 def main() -> int:
     a = _args()
+    if a.traffic_from:
+        root = os.path.dirname(os.path.abspath(__file__))
+        rec = traffic_from_counters(a.traffic_from[0], a.traffic_from[1],
+                                    a.calib_copy_mib or 256, root)
+        rec["workload"] = a.workload
+        path = _traffic_path(root, a.workload)
+        with open(path, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec))
+        return 0
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {a.gpus}); the multi-GPU decode "
               "context-parallel exchange is not part of this build", file=sys.stderr)
@@ -148,61 +202,52 @@ def main() -> int:
     out = torch.empty((w.bs, w.q_len, w.heads, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((w.bs, w.q_len, w.heads), dtype=torch.float32, device="cuda")
     max_len = int(w.seq_lens.max())
-    ev = []  # (start, end) events around each decode launch of the timed steps
+    # Per timed step, a pair of events that the decode kernel's own launch
+    # records at its begin and end (mla_decode_time_next_launch).  They are
+    # created, and recorded once so that they exist, before timing starts.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(a.steps)]
+    for e0, e1 in ev:
+        e0.record()
+        e1.record()
 
     def decode(p):
         mla.mla_decode(p.q, p.kv, bt, p.seq_lens, tile_plan, split_indptr, w.softmax_scale,
                        partial_o=po, partial_lse=pl, out=out, lse=lse, kv_dtype=w.kv_dtype,
                        kv_descale=p.kv_descale, causal=w.causal)
 
-    def step(i: int, record: bool):
+    def step(i: int, timed: int):
         p = pools[i % len(pools)]
         mla.build_block_table(p.req_to_token, p.req_pool_indices, p.seq_lens, width,
                               max_seq_len_hint=max_len, out=bt)
         mla.plan_splits(p.seq_lens, R, num_parts, w.kv_dtype, tile_plan=tile_plan,
                         split_indptr=split_indptr)
-        if record:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
+        if timed >= 0:
+            mla.time_next_decode(*ev[timed])
         decode(p)
-        if record:
-            e1.record()
-            ev.append((e0, e1))
         mla.merge_states(po, pl, split_indptr, out, lse)
 
     if a.calib_copy_mib > 0:
-        n = a.calib_copy_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        n = a.calib_copy_mib << 18  # int32 elements
+        src = torch.ones(n, dtype=torch.int32, device="cuda")
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)  # the reference kernel for FETCH_SIZE / WRITE_SIZE: n bytes each way
+        torch.bitwise_not(src, out=dst)  # reads and writes calib_copy_mib MiB
         torch.cuda.synchronize()
         del src, dst
     print(f"[bench] warmup {a.warmup} steps", file=sys.stderr, flush=True)
     for i in range(a.warmup):
-        step(i, False)
+        step(i, -1)
     torch.cuda.synchronize()
     print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
     for i in range(a.steps):
-        step(a.warmup + i, True)
+        step(a.warmup + i, i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / a.steps
-    dec_in_step_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
-    # The decode kernel's launch duration: events bracketing back-to-back
-    # launches on the stream the kernel runs on (the plan and block table of
-    # the last step are reused; the pools still rotate, so no launch finds its
-    # KV in the caches).  An event pair around a single launch also counts the
-    # dispatch and end-of-kernel fences, which this amortises away.
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(a.decode_launches):
-        decode(pools[i % len(pools)])
-    e1.record(stream)
-    torch.cuda.synchronize()
-    dec_ms = e0.elapsed_time(e1) / a.decode_launches
+    # the decode kernel's average launch duration over the timed steps
+    dec_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
 
     b = _algorithmic_bytes(w)
     kv_gbs = b["kv"] / (ms_step * 1e-3) / 1e9
@@ -236,7 +281,6 @@ def main() -> int:
         "pct_hbm_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(tokens_s, 1),
         "decode_kernel_ms": round(dec_ms, 5),
-        "decode_in_step_event_ms": round(dec_in_step_ms, 5),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),
@@ -245,8 +289,9 @@ def main() -> int:
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": _traffic(os.path.dirname(os.path.abspath(__file__)),
                                 os.path.join(os.path.dirname(os.path.abspath(__file__)),
-                                             "paged_kv_mla_req_amd", "csrc", "decode.hip")),
-            "kernel": "mla_decode_bf16_kernel",
+                                             "paged_kv_mla_req_amd", "csrc", "decode.hip"),
+                                a.workload),
+            "kernel": "mla_decode_kernel<%s>" % ("true" if w.kv_dtype != "bf16" else "false"),
             "bytes_per_launch": b["total"],
         },
     }

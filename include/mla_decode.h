@@ -168,7 +168,11 @@ int32_t mla_device_num_cus(void);
  *   tile_plan, split_indptr, num_parts   from mla_plan_splits
  *   softmax_scale host, by value (passed as a host float so no device read is
  *                 needed, as the FlashInfer page notes for graph capture)
- *   kv_descale    device fp32 scalar for fp8 (NULL for bf16)
+ *   kv_descale    device fp32 scalar delta for fp8 (ignored for bf16, may be
+ *                 NULL): the latent value of a cache byte is e4m3fn(byte) * delta,
+ *                 one scale for K and V (the page's descale_k).  delta must be
+ *                 finite; it may be 0 or negative.  Read on the device, so a
+ *                 captured graph picks up a new value without re-capture.
  *   partial_o     fp32 [partial_slots, q_len*num_heads, 512]
  *   partial_lse   fp32 [partial_slots, q_len*num_heads]
  *   out           bf16 [bs, q_len, num_heads, 512] (rows of split requests
@@ -190,6 +194,17 @@ mla_status mla_decode(const void* q, int32_t bs, int32_t q_len, int32_t num_head
                       const int32_t* split_indptr, float softmax_scale, int32_t causal,
                       const float* kv_descale, float* partial_o, float* partial_lse,
                       int32_t partial_slots, void* out, float* lse, hipStream_t stream);
+
+/*
+ * mla_decode_time_next_launch — measurement hook.  The next mla_decode call
+ * on this host thread launches its kernel with hipExtLaunchKernel so that
+ * `start` and `stop` (events the caller created; either may be NULL) take
+ * the kernel's own begin and end times.  hipEventElapsedTime(start, stop)
+ * is then the kernel's duration, without the dispatch and cache-flush time
+ * that a separate event pair around the call also counts.  The hook is used
+ * once and cleared, also when that mla_decode call fails.  Always MLA_OK.
+ */
+mla_status mla_decode_time_next_launch(hipEvent_t start, hipEvent_t stop);
 
 /*
  * mla_merge_states — exact merge of partial (o, lse) states (merge_state of

@@ -157,6 +157,14 @@ def mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tenso
         partial_o.shape[0], _p(out), _p(lse), _stream(stream)))
 
 
+def time_next_decode(start: torch.cuda.Event, stop: torch.cuda.Event) -> None:
+    """The next mla_decode on this thread records ``start``/``stop`` at its
+    kernel's own begin and end (mla_decode_time_next_launch).  The events
+    must have been recorded once before, so that they exist."""
+    _lib.check(_lib.lib().mla_decode_time_next_launch(ctypes.c_void_p(start.cuda_event),
+                                                      ctypes.c_void_p(stop.cuda_event)))
+
+
 def merge_states(partial_o: torch.Tensor, partial_lse: torch.Tensor, split_indptr: torch.Tensor,
                  out: torch.Tensor, lse: Optional[torch.Tensor] = None, stream=None) -> None:
     """Exact LSE merge of split pieces into out (bf16) and lse (mla_merge_states)."""

@@ -39,6 +39,7 @@ SIGNATURES = {
                             _c_p, _c_p, _c_i32, _c_p, _c_f32, _c_i32, _c_p, _c_p, _c_p, _c_i32,
                             _c_p, _c_p, _c_p]),
     "mla_merge_states": (_c_i32, [_c_p, _c_p, _c_p, _c_i32, _c_i32, _c_p, _c_p, _c_p]),
+    "mla_decode_time_next_launch": (_c_i32, [_c_p, _c_p]),
 }
 
 _lib = None

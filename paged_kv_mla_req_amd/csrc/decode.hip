@@ -39,8 +39,19 @@
 //  * Epilogue: an unsplit request writes bf16 o and fp32 lse; a piece of a
 //    split request writes its fp32 (o, lse) to the partial slot the planner
 //    assigned, for mla_merge_states.
+//  * fp8 cache (FlashMLA backend page, forward_decode fp8 branch; AITER
+//    helper page, forward_decode_vectorized_5d): the page holds e4m3fn bytes
+//    whose latent value is byte * delta, delta one per-tensor scale read from
+//    device memory.  A page (36 KiB) lands in one of two LDS staging buffers
+//    and the work-group converts it to bf16 -- exact, since every e4m3 value
+//    is a bf16 value -- into the single 72 KiB compute buffer, in the layout
+//    above; the MFMA work is then the bf16 work.  delta scales the scores
+//    (folded into the softmax scale, with its sign moved onto q) and the
+//    output.
 #include <cmath>
 #include <utility>
+
+#include <hip/hip_ext.h>
 
 #include "common.h"
 
@@ -60,6 +71,8 @@ constexpr int kRowsPerBlock = kWaves * kRowsPerWave;     // 128
 constexpr int kRowBytes = kD * 2;                        // 1152 bytes per bf16 latent row
 constexpr int kChunks = kRowBytes / 16;                  // 72 16-byte chunks per row
 constexpr int kPageBytes = kPage * kRowBytes;            // 73728
+constexpr int kPageBytesF8 = kPage * kD;                 // 36864: one e4m3 page
+constexpr int kLoadsPerWaveF8 = kPageBytesF8 / 1024 / kWaves;  // 9
 constexpr int kLoadsPerPage = kPageBytes / 1024;         // 72 wave-wide 1 KiB loads
 constexpr int kLoadsPerWave = kLoadsPerPage / kWaves;    // 18
 constexpr int kKSteps = kD / 16;                         // 36 MFMA k-steps for S
@@ -85,9 +98,10 @@ struct DecodeParams {
 // latent rows.  Loads past the range return zeros, so the slots of a last
 // page beyond the request's length arrive in LDS as zeros whatever the pool
 // holds there (a masked key then contributes 0 * 0, never 0 * NaN).
+template <int RowBytes>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t* page, int rows) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(page), (short)0,
-                                           rows * kRowBytes, 0x00020000);
+                                           rows * RowBytes, 0x00020000);
 }
 
 // Issue this wave's share of the direct-to-LDS loads of one page.  Load j
@@ -119,6 +133,52 @@ __device__ __forceinline__ void issue_loads(std::integer_sequence<int, K...>,
 __device__ __forceinline__ void issue_page_loads(__amdgpu_buffer_rsrc_t rsrc, uint8_t* buf,
                                                  int wave, uint32_t voff0, uint32_t voff1) {
   issue_loads(std::make_integer_sequence<int, kLoadsPerWave>{}, rsrc, buf, wave, voff0, voff1);
+}
+
+// e4m3 page: a plain copy into a 36 KiB staging buffer.  Load k of wave w
+// fills staging bytes [1024 j, 1024 j + 1024) with j = w + 4k from the same
+// page offsets; voff = 1024 w + 16 lane.
+template <int... K>
+__device__ __forceinline__ void issue_loads_f8(std::integer_sequence<int, K...>,
+                                               __amdgpu_buffer_rsrc_t rsrc, uint8_t* stage,
+                                               int wave, uint32_t voff) {
+  (__builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc,
+                                            LDS_PTR(void, stage + 1024 * (wave + kWaves * K)),
+                                            16, voff + 4096 * K, 0, 0, 0),
+   ...);
+}
+
+// Swizzle of the 16-byte chunks of key k in a column block (see the top).
+__device__ __forceinline__ int chunk_swz(int k) {
+  return 4 * ((k >> 1) & 1) + 2 * ((k >> 2) & 1) + ((k >> 4) & 1);
+}
+
+// Staged e4m3 page -> bf16 compute page.  Thread t converts key t / 4,
+// 16-byte staging chunks j = t % 4 + 4 m (columns 16 j .. 16 j + 15) for
+// m = 0..8, i.e. the chunk pair 2 (t % 4), 2 (t % 4) + 1 of column block m.
+// The conversion is exact.  All addresses are a per-thread base plus a
+// constant, so nothing is kept per m.
+__device__ __forceinline__ void convert_f8_page(const uint8_t* stage, uint8_t* buf) {
+  const int key = threadIdx.x >> 2;
+  const int c0 = 2 * (threadIdx.x & 3);
+  const int slot0 = c0 ^ chunk_swz(key);
+  const uint8_t* src = stage + key * kD + 16 * (threadIdx.x & 3);
+  uint8_t* dst0 = buf + key * 128 + (slot0 << 4);
+  uint8_t* dst1 = buf + key * 128 + ((slot0 ^ 1) << 4);
+#pragma unroll
+  for (int m = 0; m < kD / 64; ++m) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(src + 64 * m);
+    u32x4 lo, hi;
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      lo[2 * d] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[d], 1.0f, false));
+      lo[2 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[d], 1.0f, true));
+      hi[2 * d] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[d + 2], 1.0f, false));
+      hi[2 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[d + 2], 1.0f, true));
+    }
+    *reinterpret_cast<u32x4*>(dst0 + 8192 * m) = lo;
+    *reinterpret_cast<u32x4*>(dst1 + 8192 * m) = hi;
+  }
 }
 
 __device__ __forceinline__ int32_t page_count(int32_t L) {
@@ -453,15 +513,19 @@ __device__ __forceinline__ void pv_tile(f32x16 (&oacc)[kVTiles], const bf16x8 (&
   pv_chain<T>(oacc, ring, pop, va, std::make_integer_sequence<int, kPvBlocks>{});
 }
 
+// FP8: the cache holds e4m3 bytes (kv_descale is read); else bf16.
+template <bool FP8>
 __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
-mla_decode_bf16_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
-                       const int32_t* __restrict__ block_table,
-                       const int32_t* __restrict__ seq_lens,
-                       const int32_t* __restrict__ tile_plan,
-                       const int32_t* __restrict__ split_indptr, float* __restrict__ partial_o,
-                       float* __restrict__ partial_lse, uint16_t* __restrict__ out,
-                       float* __restrict__ lse_out, DecodeParams P) {
+mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
+                  const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
+                  const int32_t* __restrict__ tile_plan, const int32_t* __restrict__ split_indptr,
+                  const float* __restrict__ kv_descale, float* __restrict__ partial_o,
+                  float* __restrict__ partial_lse, uint16_t* __restrict__ out,
+                  float* __restrict__ lse_out, DecodeParams P) {
+  // bf16: two compute buffers.  fp8: compute buffer 0, and two e4m3 staging
+  // buffers in the space of compute buffer 1.
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kPageBytes];
+  constexpr int kSrcPageBytes = FP8 ? kPageBytesF8 : kPageBytes;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
@@ -492,6 +556,7 @@ mla_decode_bf16_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
       wave * (8 * kRowBytes) + (lane >> 3) * kRowBytes +
       16 * ((lane & 7) ^ (4 * ((lane >> 4) & 1) + 2 * ((lane >> 5) & 1) + ((wave >> 1) & 1)));
   const uint32_t load_voff1 = load_voff0 + 4 * (8 * kRowBytes);  // key group wave + 4
+  const uint32_t load_voff_f8 = wave * 1024 + 16 * lane;
   // S^T A operand: lane (m = n, h) reads key 32t + sigma(m) with
   // sigma(8q + 4g + t') = 16g + 4q + t', global chunk 2ks + h, i.e. column
   // block ks/4, chunk 2(ks%4) + h of the block.  Keys 32 apart share the
@@ -541,9 +606,16 @@ mla_decode_bf16_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
   };
   int64_t nphys = phys_of(nb, np);
   int nrows = min(kPage, max(0, nlen - np * kPage));
-  auto issue = [&](uint8_t* buf) {
-    issue_page_loads(page_rsrc(kv + nphys * kPageBytes, __builtin_amdgcn_readfirstlane(nrows)),
-                     buf, wave, load_voff0, load_voff1);
+  // Loads of the cursor's page into LDS for page index `j` of the part.
+  auto issue = [&](int j) {
+    const int vr = __builtin_amdgcn_readfirstlane(nrows);
+    if constexpr (FP8)
+      issue_loads_f8(std::make_integer_sequence<int, kLoadsPerWaveF8>{},
+                     page_rsrc<kD>(kv + nphys * kSrcPageBytes, vr),
+                     smem + kPageBytes + (j & 1) * kPageBytesF8, wave, load_voff_f8);
+    else
+      issue_page_loads(page_rsrc<kRowBytes>(kv + nphys * kSrcPageBytes, vr),
+                       smem + (j & 1) * kPageBytes, wave, load_voff0, load_voff1);
   };
   // Move the cursor one page on and read that page's block-table entry and
   // length.  Called after a page's compute, so the scalar loads have a whole
@@ -560,7 +632,7 @@ mla_decode_bf16_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
     nrows = min(kPage, max(0, nlen - np * kPage));
   };
 
-  issue(smem);
+  issue(0);
   advance();
 
   // Every wave passes exactly `total` barriers, one per page, whatever the
@@ -572,12 +644,22 @@ mla_decode_bf16_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
       __builtin_amdgcn_s_waitcnt(0x0f70);
       __syncthreads();
       if (it + 1 < total) {
-        issue(smem + ((it + 1) & 1) * kPageBytes);
+        issue(it + 1);
         advance();
+      }
+      if constexpr (FP8) {
+        convert_f8_page(smem + kPageBytes + (it & 1) * kPageBytesF8, smem);
+        __syncthreads();
       }
     }
     return;
   }
+
+  // Per-tensor dequantisation scale: scores use |delta| in the softmax scale
+  // and the sign on q; the output is multiplied by delta.
+  const float delta = FP8 ? kv_descale[0] : 1.0f;
+  const float c_log2 = P.scale_log2 * fabsf(delta);
+  const uint32_t q_sign = (FP8 && delta < 0.f) ? 0x80008000u : 0u;
 
   bf16x8 qreg[kKSteps];
   f32x16 oacc[kVTiles];
@@ -598,6 +680,7 @@ mla_decode_bf16_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
         u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 16 * ks);
+        if (FP8) v ^= q_sign;
         if (!row_valid) v = (u32x4){0, 0, 0, 0};
         qreg[ks] = __builtin_bit_cast(bf16x8, v);
       }
@@ -609,8 +692,12 @@ mla_decode_bf16_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
     for (; cp < cend && it < total; ++cp, ++it) {
       __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of page `it` landed
       __syncthreads();                     // ... and every wave's; buffer it+1 is free again
-      const lds_u8* base = LDS_PTR(uint8_t, smem) + (it & 1) * kPageBytes;
-      if (it + 1 < total) issue(smem + ((it + 1) & 1) * kPageBytes);
+      const lds_u8* base = LDS_PTR(uint8_t, smem) + (FP8 ? 0 : (it & 1) * kPageBytes);
+      if (it + 1 < total) issue(it + 1);
+      if constexpr (FP8) {
+        convert_f8_page(smem + kPageBytes + (it & 1) * kPageBytesF8, smem);
+        __syncthreads();  // the compute page is complete
+      }
 
       // LDS byte addresses of this page's operands
       const uint32_t pbase = (uint32_t)(uintptr_t)base;
@@ -648,7 +735,7 @@ mla_decode_bf16_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
           for (int i = 0; i < 16; i += 2) mloc = fmaxf(mloc, fmaxf(sc[i], sc[i + 1]));
         }
         mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-        const float m_tile = (mloc == -INFINITY) ? -INFINITY : P.scale_log2 * mloc;
+        const float m_tile = (mloc == -INFINITY) ? -INFINITY : c_log2 * mloc;
         const bool need = m_tile > m_run + kTau;
         if (__any(need)) {
           const float m_new = need ? m_tile : m_run;
@@ -667,7 +754,7 @@ mla_decode_bf16_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
         if (masked) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const float e = __builtin_amdgcn_exp2f(fmaf(sc[i], P.scale_log2, neg_m));
+            const float e = __builtin_amdgcn_exp2f(fmaf(sc[i], c_log2, neg_m));
             const float p = (key0 + i <= lim) ? e : 0.f;
             l_run += p;
             pop[i >> 3][i & 7] = (__bf16)p;
@@ -675,7 +762,7 @@ mla_decode_bf16_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
         } else {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(sc[i], P.scale_log2, neg_m));
+            const float p = __builtin_amdgcn_exp2f(fmaf(sc[i], c_log2, neg_m));
             l_run += p;
             pop[i >> 3][i & 7] = (__bf16)p;
           }
@@ -692,7 +779,7 @@ mla_decode_bf16_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
     // ---- epilogue of the piece ---------------------------------------------------
     {
       const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-      const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+      const float inv = l_tot > 0.f ? delta / l_tot : 0.f;
       const float lse_val =
           l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
       const int k0 = split_indptr[cb];
@@ -739,10 +826,22 @@ mla_decode_bf16_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
   for (; it < total; ++it) {
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
+    if constexpr (FP8) __syncthreads();
   }
 }
 
 }  // namespace mla
+
+namespace {
+// Events for the next launch on this thread (mla_decode_time_next_launch).
+thread_local hipEvent_t t_start_event = nullptr, t_stop_event = nullptr;
+}  // namespace
+
+extern "C" mla_status mla_decode_time_next_launch(hipEvent_t start, hipEvent_t stop) {
+  t_start_event = start;
+  t_stop_event = stop;
+  return mla::ok();
+}
 
 extern "C" mla_status mla_decode(const void* q, int32_t bs, int32_t q_len, int32_t num_heads,
                                  const void* kv_cache, int32_t kv_dtype, int64_t num_pages,
@@ -753,6 +852,8 @@ extern "C" mla_status mla_decode(const void* q, int32_t bs, int32_t q_len, int32
                                  float* partial_o, float* partial_lse, int32_t partial_slots,
                                  void* out, float* lse, hipStream_t stream) {
   using namespace mla;
+  const hipEvent_t ev_start = t_start_event, ev_stop = t_stop_event;
+  t_start_event = t_stop_event = nullptr;
   if (!q || !kv_cache || !block_table || !seq_lens || !tile_plan || !split_indptr || !partial_o ||
       !partial_lse || !out)
     return fail(MLA_ERR_INVALID_ARGUMENT, "mla_decode: null pointer");
@@ -772,8 +873,6 @@ extern "C" mla_status mla_decode(const void* q, int32_t bs, int32_t q_len, int32
     return fail(MLA_ERR_CAPACITY, "mla_decode: num_parts above " + std::to_string(MLA_MAX_PARTS));
   if ((int64_t)partial_slots < (int64_t)bs + num_parts)
     return fail(MLA_ERR_CAPACITY, "mla_decode: partial_slots must be at least bs + num_parts");
-  if (kv_dtype == MLA_KV_FP8_E4M3)
-    return fail(MLA_ERR_UNSUPPORTED, "mla_decode: fp8 cache not built yet");
 
   DecodeParams p;
   p.num_pages = num_pages;
@@ -786,9 +885,22 @@ extern "C" mla_status mla_decode(const void* q, int32_t bs, int32_t q_len, int32
   p.causal = causal ? 1 : 0;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   dim3 grid(num_parts, (unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
-  hipLaunchKernelGGL(mla_decode_bf16_kernel, grid, dim3(kWaves * 64), 0, stream,
-                     reinterpret_cast<const uint16_t*>(q), reinterpret_cast<const uint8_t*>(kv_cache),
-                     block_table, seq_lens, tile_plan, split_indptr, partial_o, partial_lse,
-                     reinterpret_cast<uint16_t*>(out), lse, p);
+  auto launch = [&](auto kernel, const float* descale) {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(q);
+    const uint8_t* kvp = reinterpret_cast<const uint8_t*>(kv_cache);
+    uint16_t* op = reinterpret_cast<uint16_t*>(out);
+    if (ev_start || ev_stop)
+      hipExtLaunchKernelGGL(kernel, grid, dim3(kWaves * 64), 0, stream, ev_start, ev_stop, 0, qp,
+                            kvp, block_table, seq_lens, tile_plan, split_indptr, descale,
+                            partial_o, partial_lse, op, lse, p);
+    else
+      hipLaunchKernelGGL(kernel, grid, dim3(kWaves * 64), 0, stream, qp, kvp, block_table,
+                         seq_lens, tile_plan, split_indptr, descale, partial_o, partial_lse, op,
+                         lse, p);
+  };
+  if (kv_dtype == MLA_KV_FP8_E4M3)
+    launch(mla_decode_kernel<true>, kv_descale);
+  else
+    launch(mla_decode_kernel<false>, nullptr);
   return check_launch("mla_decode");
 }

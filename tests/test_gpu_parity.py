@@ -234,6 +234,62 @@ def test_identical_keys_return_that_value_row(mla):
         assert np.array_equal(o[b, 0], np.broadcast_to(v, o[b, 0].shape))
 
 
+# ------------------------------------------------------------------ fp8 e4m3 cache
+
+FP8_CASES = [
+    dict(bs=3, heads=16, q_len=1, seq_lens=[1, 63, 130]),
+    dict(bs=2, heads=128, q_len=1, seq_lens=[700, 1500]),
+    dict(bs=2, heads=32, q_len=4, seq_lens=[5, 267]),        # causal verify rows
+    dict(bs=5, heads=20, q_len=1, seq_lens=[64, 1, 200, 3, 129]),
+]
+
+
+@pytest.mark.parametrize("case", FP8_CASES, ids=lambda c: f"b{c['bs']}h{c['heads']}n{c['q_len']}")
+@pytest.mark.parametrize("parts", [1, 5, 64])
+def test_fp8_small_shapes(mla, case, parts):
+    w = make_custom("f8", seed=33, kv_dtype="fp8_e4m3", **SMALL, **case)
+    o, lse = run(mla, w, num_parts=parts)
+    assert_close(o, lse, *ref(w))
+
+
+@pytest.mark.parametrize("descale_factor", [-1.0, 0.0, 3.0])
+def test_fp8_descale_sign_zero_and_size(mla, descale_factor):
+    """delta enters the scores and the output: a negative delta flips the
+    scores' sign, zero makes every visible key weigh the same (o = 0)."""
+    w = make_custom("f8d", bs=2, heads=64, q_len=2, seq_lens=[100, 333], seed=34,
+                    kv_dtype="fp8_e4m3", **SMALL)
+    w.kv_descale = float(np.float32(w.kv_descale * descale_factor))
+    o, lse = run(mla, w, num_parts=7)
+    assert_close(o, lse, *ref(w))
+
+
+@pytest.mark.parametrize("kind", ["nan", "big"])
+def test_fp8_poisoned_unused_slots_are_never_read(mla, kind):
+    w = make_custom("f8p", bs=4, heads=32, q_len=2, seq_lens=[1, 70, 129, 250], seed=35,
+                    kv_dtype="fp8_e4m3", **SMALL)
+    o1, l1 = run(mla, w, num_parts=6)
+    o2, l2 = run(mla, w, num_parts=6, kv=poison_unused(w, kind))
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    assert_close(o2, l2, *ref(w))
+
+
+def test_fp8_equals_bf16_path_on_the_same_values(mla):
+    """Every e4m3 value is a bf16 value: a bf16 cache holding dec(byte) * delta
+    with delta a power of two gives bit-identical scores, so the outputs of
+    the two kernels agree bit for bit."""
+    w8 = make_custom("f8b", bs=2, heads=128, q_len=1, seq_lens=[300, 1000], seed=36,
+                     kv_dtype="fp8_e4m3", **SMALL)
+    w8.kv_descale = 0.125
+    o8, l8 = run(mla, w8, num_parts=9)
+    wb = make_custom("f8b", bs=2, heads=128, q_len=1, seq_lens=[300, 1000], seed=36,
+                     kv_dtype="fp8_e4m3", **SMALL)
+    dec = torch.from_numpy(w8.kv).view(torch.float8_e4m3fn).float() * 0.125
+    wb.kv = dec.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    wb.kv_dtype, wb.kv_descale = "bf16", 1.0
+    ob, lb = run(mla, wb, num_parts=9)
+    assert np.array_equal(o8, ob) and np.array_equal(l8, lb)
+
+
 # ------------------------------------------------------------------ full-size, sampled rows
 
 def _sample_rows(w, per_req, seed=0):
@@ -242,7 +298,7 @@ def _sample_rows(w, per_req, seed=0):
     return {b: np.sort(rng.choice(R, size=min(per_req, R), replace=False)) for b in range(w.bs)}
 
 
-@pytest.mark.parametrize("name", ["dsv3", "dsv3_4k", "long", "verify"])
+@pytest.mark.parametrize("name", ["dsv3", "dsv3_4k", "long", "verify", "fp8"])
 def test_full_size_sampled_rows(mla, name):
     w = make_workload(name)
     o, lse = run(mla, w)           # default plan: one part per CU, as the benchmark runs
@@ -283,3 +339,26 @@ def test_merge_states_against_oracle(mla):
         assert np.all(o[b][~fin] == 0)
         np.testing.assert_allclose(o[b], mo[b], rtol=0, atol=1e-2 * max(1, np.abs(mo[b]).max()))
         np.testing.assert_allclose(l[b][fin], ml[b][fin], rtol=0, atol=1e-4 * 20)
+
+
+def test_kernel_timing_hook_records_the_launch(mla):
+    """mla_decode_time_next_launch: the events take the kernel's own begin
+    and end, the result is unchanged, and the hook is used only once."""
+    w = make_workload("tiny")
+    d = to_device(w)
+    bt = mla.build_block_table(d.req_to_token, d.req_pool_indices, d.seq_lens, w.bt_width)
+    plan = mla.plan_splits(d.seq_lens, w.rows_per_req, 3)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    e1.record()
+    torch.cuda.synchronize()
+    mla.time_next_decode(e0, e1)
+    out, lse = mla.decode(d.q, d.kv, bt, d.seq_lens, w.softmax_scale, plan=plan)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1)
+    assert 0.0 < t < 100.0
+    out2, lse2 = mla.decode(d.q, d.kv, bt, d.seq_lens, w.softmax_scale, plan=plan)
+    torch.cuda.synchronize()
+    assert e0.elapsed_time(e1) == t      # the second launch left the events alone
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    assert_close(_np(out), _np(lse), *ref(w))
