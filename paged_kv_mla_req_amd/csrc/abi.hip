@@ -18,6 +18,8 @@ mla_status ok() {
   return MLA_OK;
 }
 
+bool finite_nonneg(float x) { return std::isfinite(x) && x >= 0.f; }
+
 mla_status check_launch(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess)

@@ -19,6 +19,9 @@ mla_status fail(mla_status st, const std::string& msg);
 mla_status ok();
 // Maps the result of hipGetLastError after a launch to a status.
 mla_status check_launch(const char* what);
+// True for a finite x >= 0.  Defined in abi.hip, which keeps IEEE NaN
+// semantics (the decode kernel's file is compiled without them).
+bool finite_nonneg(float x);
 
 // fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {

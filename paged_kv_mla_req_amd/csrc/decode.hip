@@ -77,7 +77,12 @@ constexpr int kLoadsPerPage = kPageBytes / 1024;         // 72 wave-wide 1 KiB l
 constexpr int kLoadsPerWave = kLoadsPerPage / kWaves;    // 18
 constexpr int kKSteps = kD / 16;                         // 36 MFMA k-steps for S
 constexpr int kVTiles = kDv / 32;                        // 16 output tiles of 32 columns
-constexpr float kTau = 8.0f;                             // lazy-rescale threshold (log2 units)
+constexpr float kTau = 8.0f;
+// The page loop issues the next page's loads one per MFMA block: after the 9
+// score blocks and 8 output blocks of the first tile, and the first score
+// block of the second (bf16: 18 loads; e4m3: 9, all in the first score tile).
+static_assert(kLoadsPerWave == 18 && kLoadsPerWaveF8 == 9 && kKSteps / 4 == 9,
+              "load spreading assumes 18 / 9 loads and 9 score blocks");                             // lazy-rescale threshold (log2 units)
 
 // Scalar arguments of the decode kernel (pointers are kernel arguments of
 // their own, marked __restrict__, so the compiler may read the small index
@@ -148,6 +153,13 @@ __device__ __forceinline__ void issue_loads_f8(std::integer_sequence<int, K...>,
    ...);
 }
 
+template <int K>
+__device__ __forceinline__ void issue_one_load_f8(__amdgpu_buffer_rsrc_t rsrc, uint8_t* stage,
+                                                  int wave, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, stage + 1024 * (wave + kWaves * K)),
+                                           16, voff + 4096 * K, 0, 0, 0);
+}
+
 // Swizzle of the 16-byte chunks of key k in a column block (see the top).
 __device__ __forceinline__ int chunk_swz(int k) {
   return 4 * ((k >> 1) & 1) + 2 * ((k >> 2) & 1) + ((k >> 4) & 1);
@@ -183,39 +195,6 @@ __device__ __forceinline__ void convert_f8_page(const uint8_t* stage, uint8_t* b
 
 __device__ __forceinline__ int32_t page_count(int32_t L) {
   return L > 0 ? (L + kPage - 1) / kPage : 0;
-}
-
-// S^T chain on MFMA with the accumulator in VGPRs.  The output accumulator
-// (16 tiles of 16 fp32) fills all 256 AGPRs, so the score tile must live in
-// VGPRs; the compiler selects one accumulator class for every MFMA of a
-// kernel, so these MFMAs are issued from inline assembly.  Hazards the
-// compiler cannot see are covered by hand: 2 wait states before a group
-// (VALU write of an operand -> MFMA read) and 24 after the last MFMA of a
-// chain (MFMA write -> VALU read; more than the 18 a 16-pass MFMA needs).
-__device__ __forceinline__ void mfma_s4(f32x16& acc, bf16x8 a0, bf16x8 a1, bf16x8 a2, bf16x8 a3,
-                                        bf16x8 b0, bf16x8 b1, bf16x8 b2, bf16x8 b3) {
-  asm("s_nop 1\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %1, %5, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %2, %6, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %3, %7, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %4, %8, %0"
-      : "+v"(acc)
-      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(b0), "v"(b1), "v"(b2), "v"(b3));
-}
-
-__device__ __forceinline__ void mfma_s4_last(f32x16& acc, bf16x8 a0, bf16x8 a1, bf16x8 a2,
-                                             bf16x8 a3, bf16x8 b0, bf16x8 b1, bf16x8 b2,
-                                             bf16x8 b3) {
-  asm("s_nop 1\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %1, %5, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %2, %6, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %3, %7, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %4, %8, %0\n\t"
-      "s_nop 7\n\t"
-      "s_nop 7\n\t"
-      "s_nop 7"
-      : "+v"(acc)
-      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(b0), "v"(b1), "v"(b2), "v"(b3));
 }
 
 // Multiply one accumulator tile (16 AGPRs) by alpha in place, through one
@@ -341,24 +320,27 @@ __device__ __forceinline__ void s_step(f32x16& sc, bf16x8 (&kk)[2][4], const bf1
   }
 }
 
-template <int TB, int... G>
+template <int TB, typename Hook, int... G>
 __device__ __forceinline__ void s_chain(f32x16& sc, bf16x8 (&kk)[2][4],
                                         const bf16x8 (&qreg)[kKSteps], const uint32_t (&a)[4],
-                                        const uint32_t (&a_hi)[4], std::integer_sequence<int, G...>) {
-  (s_step<G, TB>(sc, kk, qreg, a, a_hi), ...);
+                                        const uint32_t (&a_hi)[4], Hook& hook,
+                                        std::integer_sequence<int, G...>) {
+  ((s_step<G, TB>(sc, kk, qreg, a, a_hi), hook(std::integral_constant<int, G>{})), ...);
 }
 
-// S^T for the 32-key tile at byte offset TB of the page: 36 MFMAs.
+// S^T for the 32-key tile at byte offset TB of the page: 36 MFMAs in 9
+// blocks; hook(integral_constant<G>) runs after block G (the page loop uses
+// it to spread the next page's global loads over the matrix work).
 // a[i] = page + koff[i] (LDS byte addresses), a_hi[i] = a[i] + 32768.
-template <int TB>
+template <int TB, typename Hook>
 __device__ __forceinline__ void score_tile(f32x16& sc, const uint32_t (&a)[4],
                                            const uint32_t (&a_hi)[4],
-                                           const bf16x8 (&qreg)[kKSteps]) {
+                                           const bf16x8 (&qreg)[kKSteps], Hook&& hook) {
   bf16x8 kk[2][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     kk[0][i] = *LDS_PTR(const bf16x8, (uintptr_t)(a[i] + TB));
-  s_chain<TB>(sc, kk, qreg, a, a_hi, std::make_integer_sequence<int, kKSteps / 4>{});
+  s_chain<TB>(sc, kk, qreg, a, a_hi, hook, std::make_integer_sequence<int, kKSteps / 4>{});
 }
 
 // PV blocks run four MFMAs each (one accumulator tile per MFMA) from a ring
@@ -462,11 +444,11 @@ __device__ __forceinline__ void pv_step(f32x16 (&oacc)[kVTiles], bf16x8 (&ring)[
   }
 }
 
-template <int T, int... B>
+template <int T, typename Hook, int... B>
 __device__ __forceinline__ void pv_chain(f32x16 (&oacc)[kVTiles], bf16x8 (&ring)[3][4],
                                          const bf16x8 (&pop)[2], const uint32_t (&va)[2][2],
-                                         std::integer_sequence<int, B...>) {
-  (pv_step<T, B>(oacc, ring, pop, va), ...);
+                                         Hook& hook, std::integer_sequence<int, B...>) {
+  ((pv_step<T, B>(oacc, ring, pop, va), hook(std::integral_constant<int, B>{})), ...);
 }
 
 // Reads of blocks 0 and 1 for tile T; returns with block 0's operands landed
@@ -504,13 +486,27 @@ __device__ __forceinline__ void pv_prologue(bf16x8 (&ring)[3][4], const uint32_t
   }
 }
 
-// O^T += V^T P^T for 32-key tile T: 32 MFMAs.  va[e][par] = page + voff.
-template <int T>
+// O^T += V^T P^T for 32-key tile T: 32 MFMAs in 8 blocks; hook runs after
+// each block, as for score_tile.  va[e][par] = page + voff.
+template <int T, typename Hook>
 __device__ __forceinline__ void pv_tile(f32x16 (&oacc)[kVTiles], const bf16x8 (&pop)[2],
-                                        const uint32_t (&va)[2][2]) {
+                                        const uint32_t (&va)[2][2], Hook&& hook) {
   bf16x8 ring[3][4];
   pv_prologue<T>(ring, va);
-  pv_chain<T>(oacc, ring, pop, va, std::make_integer_sequence<int, kPvBlocks>{});
+  pv_chain<T>(oacc, ring, pop, va, hook, std::make_integer_sequence<int, kPvBlocks>{});
+}
+
+// Max / sum over the two lane halves (which hold the same query row's other
+// keys), exchanged with v_permlane32_swap.
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // FP8: the cache holds e4m3 bytes (kv_descale is read); else bf16.
@@ -674,7 +670,8 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
     const int32_t lim = P.causal ? L - P.q_len + i_tok : L - 1;  // last visible key
     // pages from first_masked on may hold keys some row of this wave cannot see
     const int32_t lim_min = P.causal ? L - P.q_len + i_tok_min : L - 1;
-    const int first_masked = lim_min >= 0 ? (lim_min + 1) / kPage : 0;
+    const int first_masked =
+        __builtin_amdgcn_readfirstlane(lim_min >= 0 ? (lim_min + 1) / kPage : 0);
     {
       const uint16_t* qrow = q + ((int64_t)cb * P.rows + (row_valid ? r : 0)) * kD + 8 * h;
 #pragma unroll
@@ -693,7 +690,33 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
       __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of page `it` landed
       __syncthreads();                     // ... and every wave's; buffer it+1 is free again
       const lds_u8* base = LDS_PTR(uint8_t, smem) + (FP8 ? 0 : (it & 1) * kPageBytes);
-      if (it + 1 < total) issue(it + 1);
+      // The next page's loads are issued one per MFMA block (see above):
+      // issued back to back they would stall the wave until the address unit
+      // drains them.
+      const bool has_next = it + 1 < total;
+      const __amdgpu_buffer_rsrc_t next_rsrc =
+          page_rsrc<FP8 ? kD : kRowBytes>(kv + nphys * kSrcPageBytes,
+                                           __builtin_amdgcn_readfirstlane(nrows));
+      uint8_t* const next_buf = FP8 ? smem + kPageBytes + ((it + 1) & 1) * kPageBytesF8
+                                    : smem + ((it + 1) & 1) * kPageBytes;
+      // load K of this wave's share, K < 18 (bf16) or K < 9 (e4m3)
+      auto load = [&](auto kc) {
+        constexpr int K = decltype(kc)::value;
+        if (has_next) {
+          if constexpr (FP8)
+            issue_one_load_f8<K>(next_rsrc, next_buf, wave, load_voff_f8);
+          else
+            issue_one_load<K>(next_rsrc, next_buf, wave, load_voff0, load_voff1);
+        }
+      };
+      auto hook_s0 = [&](auto g) { load(g); };
+      auto hook_pv0 = [&](auto b) {
+        if constexpr (!FP8) load(std::integral_constant<int, 9 + decltype(b)::value>{});
+      };
+      auto hook_s1 = [&](auto g) {
+        if constexpr (!FP8 && decltype(g)::value == 0) load(std::integral_constant<int, 17>{});
+      };
+      auto no_hook = [](auto) {};
       if constexpr (FP8) {
         convert_f8_page(smem + kPageBytes + (it & 1) * kPageBytesF8, smem);
         __syncthreads();  // the compute page is complete
@@ -717,24 +740,30 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
         // ---- S^T = K Q^T for 32-key tile t; sc[i] is key 32t + 16h + i -----------
         f32x16 sc;
         if (t == 0)
-          score_tile<0>(sc, ka, ka_hi, qreg);
+          score_tile<0>(sc, ka, ka_hi, qreg, hook_s0);
         else
-          score_tile<32 * 128>(sc, ka, ka_hi, qreg);
+          score_tile<32 * 128>(sc, ka, ka_hi, qreg, hook_s1);
         // ---- row max of the scaled scores; weights p = 2^(c s - m) -----------------
         // c = softmax_scale * log2(e) > 0, so max(c s) = c max(s).  Keys a row
         // cannot see (causal limit, page tail) are excluded on the pages
         // where they can occur.
         const int key0 = cp * kPage + 32 * t + 16 * h;
         const bool masked = cp >= first_masked;
-        float mloc = -INFINITY;
+        float mx[4];
         if (masked) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, (key0 + i <= lim) ? sc[i] : -INFINITY);
+          for (int j = 0; j < 4; ++j) {
+            mx[j] = -INFINITY;
+#pragma unroll
+            for (int i = j; i < 16; i += 4)
+              mx[j] = fmaxf(mx[j], (key0 + i <= lim) ? sc[i] : -INFINITY);
+          }
         } else {
 #pragma unroll
-          for (int i = 0; i < 16; i += 2) mloc = fmaxf(mloc, fmaxf(sc[i], sc[i + 1]));
+          for (int j = 0; j < 4; ++j)
+            mx[j] = fmaxf(fmaxf(sc[j], sc[j + 4]), fmaxf(sc[j + 8], sc[j + 12]));
         }
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+        const float mloc = xhalf_max(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])));
         const float m_tile = (mloc == -INFINITY) ? -INFINITY : c_log2 * mloc;
         const bool need = m_tile > m_run + kTau;
         if (__any(need)) {
@@ -751,34 +780,36 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
         }
         const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
         bf16x8 pop[2];
+        float ls[4] = {0.f, 0.f, 0.f, 0.f};
         if (masked) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const float e = __builtin_amdgcn_exp2f(fmaf(sc[i], c_log2, neg_m));
             const float p = (key0 + i <= lim) ? e : 0.f;
-            l_run += p;
+            ls[i & 3] += p;
             pop[i >> 3][i & 7] = (__bf16)p;
           }
         } else {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const float p = __builtin_amdgcn_exp2f(fmaf(sc[i], c_log2, neg_m));
-            l_run += p;
+            ls[i & 3] += p;
             pop[i >> 3][i & 7] = (__bf16)p;
           }
         }
+        l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
         // ---- O^T += V^T P^T ------------------------------------------------------------
         if (t == 0)
-          pv_tile<0>(oacc, pop, va);
+          pv_tile<0>(oacc, pop, va, hook_pv0);
         else
-          pv_tile<1>(oacc, pop, va);
+          pv_tile<1>(oacc, pop, va, no_hook);
       }
       if (it + 1 < total) advance();
     }
 
     // ---- epilogue of the piece ---------------------------------------------------
     {
-      const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+      const float l_tot = xhalf_sum(l_run);
       const float inv = l_tot > 0.f ? delta / l_tot : 0.f;
       const float lse_val =
           l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
@@ -860,7 +891,7 @@ extern "C" mla_status mla_decode(const void* q, int32_t bs, int32_t q_len, int32
   if (bs <= 0 || q_len <= 0 || num_heads <= 0 || num_pages <= 0 || bt_row_stride <= 0 ||
       num_parts <= 0)
     return fail(MLA_ERR_INVALID_ARGUMENT, "mla_decode: sizes must be positive");
-  if (!std::isfinite(softmax_scale) || softmax_scale < 0.f)
+  if (!finite_nonneg(softmax_scale))
     return fail(MLA_ERR_INVALID_ARGUMENT, "mla_decode: softmax_scale must be finite and >= 0");
   if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3)
     return fail(MLA_ERR_UNSUPPORTED, "mla_decode: unknown kv_dtype");
