@@ -61,6 +61,8 @@ typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -235,188 +237,163 @@ __device__ __forceinline__ void scale_tile(f32x16& acc, float alpha) {
 }
 
 // ---------------------------------------------------------------------------
-// The two MFMA chains of a page are issued from inline assembly in blocks of
-// four MFMAs.  Each block first issues the LDS reads of the *next* block's
-// operands, then its own MFMAs, then waits for those reads: the reads are
-// always in flight behind 128 cycles of matrix work, and no register leaves
-// a block with a load still pending, so the compiler may move or copy any
-// block output freely.  (Left to itself the compiler sinks every read next
-// to its MFMA, because the kernel sits at the 512-register limit.)
+// The two MFMA chains of a page are issued from inline assembly, one MFMA
+// per statement, with compiler scheduling barriers between statements so
+// that the order written here is the order issued:
+//  * LDS operand reads for a later group of four MFMAs are issued before the
+//    current group, so they are in flight behind its matrix work (left to
+//    itself the compiler would sink every read next to its MFMA, since the
+//    kernel sits at the 512-register limit);
+//  * after every MFMA a payload slot runs caller code (VALU work of the
+//    softmax) in the shadow of the matrix pipe, and after every group a hook
+//    (the next page's global loads);
+//  * the waits for the reads are statements that take the read registers
+//    as in/out operands, so no use of them can be placed above the wait.
 // Hazards the compiler cannot see are covered by hand: 2 wait states before
-// the MFMAs of a block (a VALU write of an operand just before), and 24
-// after the last MFMA of a chain (MFMA result -> VALU / accumulator read;
-// more than the 18 a 16-pass MFMA needs).
+// each MFMA (a VALU write of an operand just before), and 24 after the last
+// MFMA of a chain (MFMA result -> VALU or accumulator read; more than a
+// 16-pass MFMA needs).
 // ---------------------------------------------------------------------------
+#define MLA_SB() __builtin_amdgcn_sched_barrier(0)
 
-// S^T block: reads K operands at a[i] + OFF into nk, then 4 MFMAs on k.
-template <int OFF>
-__device__ __forceinline__ void s_block(f32x16& sc, bf16x8 (&nk)[4], const bf16x8 (&k)[4],
-                                        const bf16x8* q, const uint32_t (&a)[4]) {
-  asm volatile(
-      "ds_read_b128 %1, %13 offset:%17\n\t"
-      "ds_read_b128 %2, %14 offset:%17\n\t"
-      "ds_read_b128 %3, %15 offset:%17\n\t"
-      "ds_read_b128 %4, %16 offset:%17\n\t"
-      "s_nop 1\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %5, %9, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %6, %10, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %7, %11, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %8, %12, %0\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "+v"(sc), "=&v"(nk[0]), "=&v"(nk[1]), "=&v"(nk[2]), "=&v"(nk[3])
-      : "v"(k[0]), "v"(k[1]), "v"(k[2]), "v"(k[3]), "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]),
-        "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF));
+template <int N>
+using ic = std::integral_constant<int, N>;
+
+// Pins values to a point of the instruction stream: an empty volatile
+// statement that claims to modify them.  Payload code reads its inputs
+// through one and hands its results to one, so the compiler can move it
+// neither above nor below its slot (scheduling barriers alone do not stop
+// sinking of pure arithmetic into later blocks).
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
+
+struct NoSlot {
+  template <int N>
+  __device__ __forceinline__ void operator()(ic<N>) const {}
+};
+
+// S^T MFMA with the accumulator in VGPRs (the output accumulator takes all
+// 256 AGPRs); FIRST starts from zero.
+template <bool FIRST>
+__device__ __forceinline__ void mfma_s(f32x16& c, const bf16x8& a, const bf16x8& b) {
+  if constexpr (FIRST)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+                 : "=&v"(c)
+                 : "v"(a), "v"(b));
+  else
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                 : "+v"(c)
+                 : "v"(a), "v"(b));
 }
 
-// First S^T block of a tile: the accumulator starts from 0.
-template <int OFF>
-__device__ __forceinline__ void s_block_first(f32x16& sc, bf16x8 (&nk)[4], const bf16x8 (&k)[4],
-                                              const bf16x8* q, const uint32_t (&a)[4]) {
-  asm volatile(
-      "ds_read_b128 %1, %13 offset:%17\n\t"
-      "ds_read_b128 %2, %14 offset:%17\n\t"
-      "ds_read_b128 %3, %15 offset:%17\n\t"
-      "ds_read_b128 %4, %16 offset:%17\n\t"
-      "s_nop 1\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %5, %9, 0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %6, %10, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %7, %11, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %8, %12, %0\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(sc), "=&v"(nk[0]), "=&v"(nk[1]), "=&v"(nk[2]), "=&v"(nk[3])
-      : "v"(k[0]), "v"(k[1]), "v"(k[2]), "v"(k[3]), "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]),
-        "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF));
+// O^T MFMA, accumulator tile in AGPRs.
+__device__ __forceinline__ void mfma_o(f32x16& o, const bf16x8& v, const bf16x8& p) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(v), "v"(p));
 }
 
-// Last S^T block: no further reads; the result is read by VALU next.
-__device__ __forceinline__ void s_block_last(f32x16& sc, const bf16x8 (&k)[4], const bf16x8* q) {
-  asm volatile(
-      "s_nop 1\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %1, %5, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %2, %6, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %3, %7, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %4, %8, %0\n\t"
-      "s_nop 7\n\t"
-      "s_nop 7\n\t"
-      "s_nop 7"
-      : "+v"(sc)
-      : "v"(k[0]), "v"(k[1]), "v"(k[2]), "v"(k[3]), "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]));
-}
+__device__ __forceinline__ void mfma_tail() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
 
-// a[i] for column blocks >= 8: the DS offset field stops at 65535.
-template <int G, int TB>
-__device__ __forceinline__ void s_step(f32x16& sc, bf16x8 (&kk)[2][4], const bf16x8 (&qreg)[kKSteps],
-                                       const uint32_t (&a)[4], const uint32_t (&a_hi)[4]) {
-  constexpr int NOFF = 8192 * (G + 1) + TB;  // byte offset of the next group's reads
-  if constexpr (G == 0)
-    s_block_first<NOFF>(sc, kk[1], kk[0], &qreg[0], a);
-  else if constexpr (G + 1 < kKSteps / 4) {
-    if constexpr (NOFF < 65536)
-      s_block<NOFF>(sc, kk[(G + 1) & 1], kk[G & 1], &qreg[4 * G], a);
-    else
-      s_block<NOFF - 32768>(sc, kk[(G + 1) & 1], kk[G & 1], &qreg[4 * G], a_hi);
+// S^T chain: one 16-byte K-operand read per MFMA, from a ring of kKRing
+// operand slots.  The read for k-step ks+kKAhead is issued right after
+// MFMA ks, into the slot MFMA ks-1 used (its operands were read when it
+// issued, a full MFMA earlier), and MFMA ks+1 first waits until its own
+// read has landed -- so every read has about kKAhead MFMAs (~230 cycles) to
+// arrive, with one wait per MFMA.
+constexpr int kKRing = 8;
+constexpr int kKAhead = kKRing - 1;
+
+// K operand of k-step KS of the tile at byte offset TB: 16 bytes at
+// a[KS % 4] + 8192 (KS / 4) + TB (column block KS / 4).  Column block 8 lies
+// past the DS offset field (65535): its address is moved up by 32 KiB first.
+template <int TB, int KS>
+__device__ __forceinline__ void k_read(bf16x8& dst, const uint32_t (&a)[4]) {
+  constexpr int OFF = 8192 * (KS / 4) + TB;
+  if constexpr (OFF < 65536) {
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=&v"(dst) : "v"(a[KS % 4]), "i"(OFF));
   } else {
-    s_block_last(sc, kk[G & 1], &qreg[4 * G]);
+    uint32_t t;
+    asm volatile("v_add_u32 %1, 0x8000, %2\n\tds_read_b128 %0, %1 offset:%3"
+                 : "=&v"(dst), "=&v"(t)
+                 : "v"(a[KS % 4]), "i"(OFF - 32768));
   }
 }
 
-template <int TB, typename Hook, int... G>
-__device__ __forceinline__ void s_chain(f32x16& sc, bf16x8 (&kk)[2][4],
+// Wait until at most N LDS reads are outstanding; x is usable after it.
+template <int N>
+__device__ __forceinline__ void lds_wait(bf16x8& x) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "i"(N));
+}
+
+// Step KS of the S^T chain of the tile at TB: MFMA KS, payload slot KS, the
+// read for KS + kKAhead, the wait for KS + 1, and hook(KS / 4) after every
+// fourth MFMA (the waits leave no read in flight across a hook only at the
+// end of the chain, so hooks must not touch LDS reads).
+template <int TB, int KS, typename Hook, typename Pay>
+__device__ __forceinline__ void s_step(f32x16& sc, bf16x8 (&ring)[kKRing],
+                                       const bf16x8 (&qreg)[kKSteps], const uint32_t (&a)[4],
+                                       Hook& hook, Pay& pay) {
+  mfma_s<KS == 0>(sc, ring[KS % kKRing], qreg[KS]);
+  MLA_SB();
+  pay(ic<KS>{});
+  MLA_SB();
+  if constexpr (KS + kKAhead < kKSteps) k_read<TB, KS + kKAhead>(ring[(KS + kKAhead) % kKRing], a);
+  MLA_SB();
+  if constexpr (KS + 1 < kKSteps) {
+    // reads issued after the one for KS + 1: KS + 2 .. min(KS + kKAhead, last)
+    constexpr int last = (KS + kKAhead < kKSteps) ? KS + kKAhead : kKSteps - 1;
+    lds_wait<last - (KS + 1)>(ring[(KS + 1) % kKRing]);
+  } else {
+    mfma_tail();
+  }
+  MLA_SB();
+  if constexpr (KS % 4 == 3) {
+    hook(ic<KS / 4>{});
+    MLA_SB();
+  }
+}
+
+template <int TB, typename Hook, typename Pay, int... KS>
+__device__ __forceinline__ void s_steps(f32x16& sc, bf16x8 (&ring)[kKRing],
                                         const bf16x8 (&qreg)[kKSteps], const uint32_t (&a)[4],
-                                        const uint32_t (&a_hi)[4], Hook& hook,
-                                        std::integer_sequence<int, G...>) {
-  ((s_step<G, TB>(sc, kk, qreg, a, a_hi), hook(std::integral_constant<int, G>{})), ...);
+                                        Hook& hook, Pay& pay, std::integer_sequence<int, KS...>) {
+  (s_step<TB, KS>(sc, ring, qreg, a, hook, pay), ...);
 }
 
-// S^T for the 32-key tile at byte offset TB of the page: 36 MFMAs in 9
-// blocks; hook(integral_constant<G>) runs after block G (the page loop uses
-// it to spread the next page's global loads over the matrix work).
-// a[i] = page + koff[i] (LDS byte addresses), a_hi[i] = a[i] + 32768.
-template <int TB, typename Hook>
-__device__ __forceinline__ void score_tile(f32x16& sc, const uint32_t (&a)[4],
-                                           const uint32_t (&a_hi)[4],
-                                           const bf16x8 (&qreg)[kKSteps], Hook&& hook) {
-  bf16x8 kk[2][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    kk[0][i] = *LDS_PTR(const bf16x8, (uintptr_t)(a[i] + TB));
-  s_chain<TB>(sc, kk, qreg, a, a_hi, hook, std::make_integer_sequence<int, kKSteps / 4>{});
+template <int TB, int... KS>
+__device__ __forceinline__ void s_prologue(bf16x8 (&ring)[kKRing], const uint32_t (&a)[4],
+                                           std::integer_sequence<int, KS...>) {
+  (k_read<TB, KS>(ring[KS], a), ...);
 }
 
-// PV blocks run four MFMAs each (one accumulator tile per MFMA) from a ring
-// of three operand sets: block b computes with set b % 3 and issues the reads
-// of block b + 2 into set (b + 2) % 3, then waits until at most those eight
-// reads are outstanding, i.e. until block b + 1's operands have landed.  The
-// reads of a block therefore have two blocks (256 cycles) of matrix work to
-// arrive.  Set (b + 2) % 3 is an output of block b but is first read by
-// block b + 2, after block b + 1 has waited for it.
-// V^T operand reads of one MFMA: two transposing 8-byte reads (keys
-// kb..kb+3 and kb+4..kb+7) at va[0][par] + off and va[1][par] + off.
-#define MLA_PV_READS                                   \
-  "ds_read_b64_tr_b16 %4, %17 offset:%21\n\t"          \
-  "ds_read_b64_tr_b16 %8, %18 offset:%21\n\t"          \
-  "ds_read_b64_tr_b16 %5, %19 offset:%21\n\t"          \
-  "ds_read_b64_tr_b16 %9, %20 offset:%21\n\t"          \
-  "ds_read_b64_tr_b16 %6, %17 offset:%22\n\t"          \
-  "ds_read_b64_tr_b16 %10, %18 offset:%22\n\t"         \
-  "ds_read_b64_tr_b16 %7, %19 offset:%22\n\t"          \
-  "ds_read_b64_tr_b16 %11, %20 offset:%22\n\t"
-
-// Block with reads ahead.  WAIT is the number of LDS reads allowed to stay
-// outstanding at the end (8: the ones just issued).
-template <int OFF0, int OFF1, int WAIT>
-__device__ __forceinline__ void pv_block_rd(f32x16& o0, f32x16& o1, f32x16& o2, f32x16& o3,
-                                            bf16x4 (&nlo)[4], bf16x4 (&nhi)[4],
-                                            const bf16x8 (&v)[4], bf16x8 p,
-                                            const uint32_t (&va)[2][2]) {
-  asm volatile(
-      MLA_PV_READS
-      "s_nop 1\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %12, %16, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %1, %13, %16, %1\n\t"
-      "v_mfma_f32_32x32x16_bf16 %2, %14, %16, %2\n\t"
-      "v_mfma_f32_32x32x16_bf16 %3, %15, %16, %3\n\t"
-      "s_waitcnt lgkmcnt(%23)"
-      : "+a"(o0), "+a"(o1), "+a"(o2), "+a"(o3), "=&v"(nlo[0]), "=&v"(nlo[1]), "=&v"(nlo[2]),
-        "=&v"(nlo[3]), "=&v"(nhi[0]), "=&v"(nhi[1]), "=&v"(nhi[2]), "=&v"(nhi[3])
-      : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(p), "v"(va[0][0]), "v"(va[1][0]),
-        "v"(va[0][1]), "v"(va[1][1]), "i"(OFF0), "i"(OFF1), "i"(WAIT));
+// S^T for the 32-key tile at byte offset TB of the page: 36 MFMAs.
+// pay(ic<s>) runs after MFMA s (0..35), hook(ic<G>) after MFMA 4G+3.
+// ka0 = page + the lane's K offset for 16-byte chunk 0 (LDS byte address);
+// chunk i of the lane's k-step is at ka0 ^ 32 i (see the swizzle above).
+template <int TB, typename Hook, typename Pay>
+__device__ __forceinline__ void score_tile(f32x16& sc, uint32_t ka0,
+                                           const bf16x8 (&qreg)[kKSteps], Hook&& hook,
+                                           Pay&& pay) {
+  const uint32_t a[4] = {ka0, ka0 ^ 32u, ka0 ^ 64u, ka0 ^ 96u};
+  bf16x8 ring[kKRing];
+  s_prologue<TB>(ring, a, std::make_integer_sequence<int, kKAhead>{});
+  lds_wait<kKAhead - 1>(ring[0]);
+  MLA_SB();
+  s_steps<TB>(sc, ring, qreg, a, hook, pay, std::make_integer_sequence<int, kKSteps>{});
 }
 
-// Block without reads; WAIT as above (0: drain), LAST adds the tail that
-// lets VALU read the accumulators next.
-template <int WAIT, bool LAST>
-__device__ __forceinline__ void pv_block_nord(f32x16& o0, f32x16& o1, f32x16& o2, f32x16& o3,
-                                              const bf16x8 (&v)[4], bf16x8 p) {
-  if constexpr (LAST)
-    asm volatile(
-        "s_nop 1\n\t"
-        "v_mfma_f32_32x32x16_bf16 %0, %4, %8, %0\n\t"
-        "v_mfma_f32_32x32x16_bf16 %1, %5, %8, %1\n\t"
-        "v_mfma_f32_32x32x16_bf16 %2, %6, %8, %2\n\t"
-        "v_mfma_f32_32x32x16_bf16 %3, %7, %8, %3\n\t"
-        "s_nop 7\n\t"
-        "s_nop 7\n\t"
-        "s_nop 7"
-        : "+a"(o0), "+a"(o1), "+a"(o2), "+a"(o3)
-        : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(p));
-  else
-    asm volatile(
-        "s_nop 1\n\t"
-        "v_mfma_f32_32x32x16_bf16 %0, %4, %8, %0\n\t"
-        "v_mfma_f32_32x32x16_bf16 %1, %5, %8, %1\n\t"
-        "v_mfma_f32_32x32x16_bf16 %2, %6, %8, %2\n\t"
-        "v_mfma_f32_32x32x16_bf16 %3, %7, %8, %3\n\t"
-        "s_waitcnt lgkmcnt(%9)"
-        : "+a"(o0), "+a"(o1), "+a"(o2), "+a"(o3)
-        : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(p), "i"(WAIT));
-}
+// The output chain of a 32-key tile: 32 MFMAs (16 accumulator tiles x two
+// 16-key steps) in 8 groups of 4.  V^T operands come from three rotating
+// sets: group b uses set b % 3 and issues the reads of group b + 2 into set
+// (b + 2) % 3, then waits until at most those eight reads are outstanding,
+// i.e. until group b + 1's set has landed; each read has two groups (256
+// cycles) of matrix work to arrive.  An operand is two transposing 8-byte
+// reads (keys kb..kb+3 and kb+4..kb+7 of the lane half) at va[0][par] + off
+// and va[1][par] + off.
+constexpr int kPvBlocks = 2 * kVTiles / 4;  // 8 groups of 4 MFMAs per 32-key tile
 
-constexpr int kPvBlocks = 2 * kVTiles / 4;  // 8 blocks of 4 MFMAs per 32-key tile
-
-// LDS offsets (relative to va) of block nb's reads: MFMA i = 4 nb + j has
+// LDS offsets (relative to va) of group nb's reads: MFMA i = 4 nb + j has
 // u = i / 16 (keys 8u..8u+7 of the lane half) and vt = i % 16; MFMAs j = 0, 1
-// share column block vt/2 (OFF0), j = 2, 3 the next one (OFF1).
+// share column block vt/2 (off0), j = 2, 3 the next one (off1).
 template <int T, int NB>
 struct PvOff {
   static constexpr int n0 = 4 * NB, nu = n0 / kVTiles, nvt = n0 % kVTiles;
@@ -425,75 +402,87 @@ struct PvOff {
   static constexpr int off1 = row + 8192 * ((nvt + 2) >> 1);
 };
 
-template <int T, int B>
-__device__ __forceinline__ void pv_step(f32x16 (&oacc)[kVTiles], bf16x8 (&ring)[3][4],
-                                        const bf16x8 (&pop)[2], const uint32_t (&va)[2][2]) {
-  constexpr int u = (4 * B) / kVTiles, vt0 = (4 * B) % kVTiles;
-  bf16x8(&cur)[4] = ring[B % 3];
-  if constexpr (B + 2 < kPvBlocks) {
-    bf16x4 nlo[4], nhi[4];
-    pv_block_rd<PvOff<T, B + 2>::off0, PvOff<T, B + 2>::off1, 8>(
-        oacc[vt0], oacc[vt0 + 1], oacc[vt0 + 2], oacc[vt0 + 3], nlo, nhi, cur, pop[u], va);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      ring[(B + 2) % 3][j] = __builtin_shufflevector(nlo[j], nhi[j], 0, 1, 2, 3, 4, 5, 6, 7);
-  } else if constexpr (B + 1 < kPvBlocks) {
-    pv_block_nord<0, false>(oacc[vt0], oacc[vt0 + 1], oacc[vt0 + 2], oacc[vt0 + 3], cur, pop[u]);
-  } else {
-    pv_block_nord<0, true>(oacc[vt0], oacc[vt0 + 1], oacc[vt0 + 2], oacc[vt0 + 3], cur, pop[u]);
-  }
-}
+struct VSet {
+  bf16x4 lo[4], hi[4];
+};
 
-template <int T, typename Hook, int... B>
-__device__ __forceinline__ void pv_chain(f32x16 (&oacc)[kVTiles], bf16x8 (&ring)[3][4],
-                                         const bf16x8 (&pop)[2], const uint32_t (&va)[2][2],
-                                         Hook& hook, std::integer_sequence<int, B...>) {
-  ((pv_step<T, B>(oacc, ring, pop, va), hook(std::integral_constant<int, B>{})), ...);
-}
-
-// Reads of blocks 0 and 1 for tile T; returns with block 0's operands landed
-// and block 1's eight reads possibly outstanding.
-template <int T>
-__device__ __forceinline__ void pv_prologue(bf16x8 (&ring)[3][4], const uint32_t (&va)[2][2]) {
-  bf16x4 lo0[4], hi0[4], lo1[4], hi1[4];
+template <int T, int NB>
+__device__ __forceinline__ void v_reads(VSet& s, const uint32_t (&va)[2][2]) {
   asm volatile(
-      "ds_read_b64_tr_b16 %0, %16 offset:%20\n\t"
-      "ds_read_b64_tr_b16 %4, %17 offset:%20\n\t"
-      "ds_read_b64_tr_b16 %1, %18 offset:%20\n\t"
-      "ds_read_b64_tr_b16 %5, %19 offset:%20\n\t"
-      "ds_read_b64_tr_b16 %2, %16 offset:%21\n\t"
-      "ds_read_b64_tr_b16 %6, %17 offset:%21\n\t"
-      "ds_read_b64_tr_b16 %3, %18 offset:%21\n\t"
-      "ds_read_b64_tr_b16 %7, %19 offset:%21\n\t"
-      "ds_read_b64_tr_b16 %8, %16 offset:%22\n\t"
-      "ds_read_b64_tr_b16 %12, %17 offset:%22\n\t"
-      "ds_read_b64_tr_b16 %9, %18 offset:%22\n\t"
-      "ds_read_b64_tr_b16 %13, %19 offset:%22\n\t"
-      "ds_read_b64_tr_b16 %10, %16 offset:%23\n\t"
-      "ds_read_b64_tr_b16 %14, %17 offset:%23\n\t"
-      "ds_read_b64_tr_b16 %11, %18 offset:%23\n\t"
-      "ds_read_b64_tr_b16 %15, %19 offset:%23\n\t"
-      "s_waitcnt lgkmcnt(8)"
-      : "=&v"(lo0[0]), "=&v"(lo0[1]), "=&v"(lo0[2]), "=&v"(lo0[3]), "=&v"(hi0[0]), "=&v"(hi0[1]),
-        "=&v"(hi0[2]), "=&v"(hi0[3]), "=&v"(lo1[0]), "=&v"(lo1[1]), "=&v"(lo1[2]),
-        "=&v"(lo1[3]), "=&v"(hi1[0]), "=&v"(hi1[1]), "=&v"(hi1[2]), "=&v"(hi1[3])
-      : "v"(va[0][0]), "v"(va[1][0]), "v"(va[0][1]), "v"(va[1][1]), "i"(PvOff<T, 0>::off0),
-        "i"(PvOff<T, 0>::off1), "i"(PvOff<T, 1>::off0), "i"(PvOff<T, 1>::off1));
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    ring[0][j] = __builtin_shufflevector(lo0[j], hi0[j], 0, 1, 2, 3, 4, 5, 6, 7);
-    ring[1][j] = __builtin_shufflevector(lo1[j], hi1[j], 0, 1, 2, 3, 4, 5, 6, 7);
-  }
+      "ds_read_b64_tr_b16 %[l0], %[a00] offset:%[o0]\n\t"
+      "ds_read_b64_tr_b16 %[h0], %[a10] offset:%[o0]\n\t"
+      "ds_read_b64_tr_b16 %[l1], %[a01] offset:%[o0]\n\t"
+      "ds_read_b64_tr_b16 %[h1], %[a11] offset:%[o0]\n\t"
+      "ds_read_b64_tr_b16 %[l2], %[a00] offset:%[o1]\n\t"
+      "ds_read_b64_tr_b16 %[h2], %[a10] offset:%[o1]\n\t"
+      "ds_read_b64_tr_b16 %[l3], %[a01] offset:%[o1]\n\t"
+      "ds_read_b64_tr_b16 %[h3], %[a11] offset:%[o1]"
+      : [l0] "=&v"(s.lo[0]), [l1] "=&v"(s.lo[1]), [l2] "=&v"(s.lo[2]), [l3] "=&v"(s.lo[3]),
+        [h0] "=&v"(s.hi[0]), [h1] "=&v"(s.hi[1]), [h2] "=&v"(s.hi[2]), [h3] "=&v"(s.hi[3])
+      : [a00] "v"(va[0][0]), [a10] "v"(va[1][0]), [a01] "v"(va[0][1]), [a11] "v"(va[1][1]),
+        [o0] "i"(PvOff<T, NB>::off0), [o1] "i"(PvOff<T, NB>::off1));
 }
 
-// O^T += V^T P^T for 32-key tile T: 32 MFMAs in 8 blocks; hook runs after
-// each block, as for score_tile.  va[e][par] = page + voff.
-template <int T, typename Hook>
+// Wait until at most N LDS reads are outstanding; s becomes usable after it.
+template <int N>
+__device__ __forceinline__ void v_wait(VSet& s) {
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+v"(s.lo[0]), "+v"(s.lo[1]), "+v"(s.lo[2]), "+v"(s.lo[3]), "+v"(s.hi[0]),
+                 "+v"(s.hi[1]), "+v"(s.hi[2]), "+v"(s.hi[3])
+               : "i"(N));
+}
+
+// MFMA J of group B of an output chain, then payload slot 4B+J.
+template <int B, int J, typename Pay>
+__device__ __forceinline__ void pv_mfma(f32x16 (&oacc)[kVTiles], const VSet& s,
+                                        const bf16x8 (&pop)[2], Pay& pay) {
+  constexpr int u = (4 * B) / kVTiles, vt = (4 * B) % kVTiles + J;
+  mfma_o(oacc[vt], __builtin_shufflevector(s.lo[J], s.hi[J], 0, 1, 2, 3, 4, 5, 6, 7), pop[u]);
+  MLA_SB();
+  pay(ic<4 * B + J>{});
+  MLA_SB();
+}
+
+template <int T, int B, typename Hook, typename Pay, int... J>
+__device__ __forceinline__ void pv_group(f32x16 (&oacc)[kVTiles], VSet (&ring)[3],
+                                         const bf16x8 (&pop)[2], const uint32_t (&va)[2][2],
+                                         Hook& hook, Pay& pay, std::integer_sequence<int, J...>) {
+  if constexpr (B + 2 < kPvBlocks) v_reads<T, B + 2>(ring[(B + 2) % 3], va);
+  MLA_SB();
+  (pv_mfma<B, J>(oacc, ring[B % 3], pop, pay), ...);
+  if constexpr (B + 2 < kPvBlocks)
+    v_wait<8>(ring[(B + 1) % 3]);
+  else if constexpr (B + 1 < kPvBlocks)
+    v_wait<0>(ring[(B + 1) % 3]);
+  else
+    mfma_tail();
+  MLA_SB();
+  hook(ic<B>{});
+  MLA_SB();
+}
+
+template <int T, typename Hook, typename Pay, int... B>
+__device__ __forceinline__ void pv_chain(f32x16 (&oacc)[kVTiles], VSet (&ring)[3],
+                                         const bf16x8 (&pop)[2], const uint32_t (&va)[2][2],
+                                         Hook& hook, Pay& pay, std::integer_sequence<int, B...>) {
+  (pv_group<T, B>(oacc, ring, pop, va, hook, pay, std::make_integer_sequence<int, 4>{}), ...);
+}
+
+// O^T += V^T P^T for 32-key tile T: 32 MFMAs.  pay(ic<s>) runs after MFMA s
+// (0..31), hook(ic<B>) after group B.  va0 = page + the lane's V offset for
+// (e, par) = (0, 0); the others follow from the swizzle:
+// (0, 1) = va0 ^ 64, (1, 0) = (va0 + 512) ^ 32, (1, 1) = that ^ 64.
+template <int T, typename Hook, typename Pay>
 __device__ __forceinline__ void pv_tile(f32x16 (&oacc)[kVTiles], const bf16x8 (&pop)[2],
-                                        const uint32_t (&va)[2][2], Hook&& hook) {
-  bf16x8 ring[3][4];
-  pv_prologue<T>(ring, va);
-  pv_chain<T>(oacc, ring, pop, va, hook, std::make_integer_sequence<int, kPvBlocks>{});
+                                        uint32_t va0, Hook&& hook, Pay&& pay) {
+  const uint32_t va10 = (va0 + 512u) ^ 32u;
+  const uint32_t va[2][2] = {{va0, va0 ^ 64u}, {va10, va10 ^ 64u}};
+  VSet ring[3];
+  v_reads<T, 0>(ring[0], va);
+  v_reads<T, 1>(ring[1], va);
+  v_wait<8>(ring[0]);
+  MLA_SB();
+  pv_chain<T>(oacc, ring, pop, va, hook, pay, std::make_integer_sequence<int, kPvBlocks>{});
 }
 
 // Max / sum over the two lane halves (which hold the same query row's other
@@ -507,6 +496,46 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Per-lane constants of the page loop.  The loop runs at the 512-register
+// limit, so these are recomputed from a pinned lane id (a few VALU
+// instructions) where they are needed rather than held in registers, which
+// the compiler would spill and reload with a wait on all vector memory.
+struct LaneOffsets {
+  uint32_t k;     // S^T A operand: LDS offset of the lane's 16-byte chunk 0
+  uint32_t v;     // V^T A operand: LDS offset for (e, par) = (0, 0)
+  uint32_t load;  // bf16 page load, key group = wave: global (= LDS source) offset
+};
+
+__device__ __forceinline__ uint32_t pinned_lane() {
+  uint32_t l = threadIdx.x & 63;
+  pin(l);
+  return l;
+}
+
+__device__ __forceinline__ LaneOffsets lane_offsets(uint32_t lane, int wave) {
+  LaneOffsets o;
+  const int n = lane & 31, h = lane >> 5;
+  // S^T A operand: lane (m = n, h) reads key 32t + sigma(m) with
+  // sigma(8q + 4g + t') = 16g + 4q + t', global chunk 2ks + h, i.e. column
+  // block ks/4, chunk 2(ks%4) + h of the block.  Keys 32 apart share the
+  // swizzle, so tile 1 is tile 0 plus 32 rows of 128 bytes; chunk i of the
+  // lane's k-step is at o.k ^ 32 i.
+  const int sig = 16 * ((n >> 2) & 1) + 4 * (n >> 3) + (n & 3);
+  o.k = sig * 128 + ((h ^ chunk_swz(sig)) << 4);
+  // V^T A operand via ds_read_b64_tr_b16: in the 16-lane block (c16, s16)
+  // of half h, source lane s16 addresses key kb + 4e + s16/4 (kb a multiple
+  // of 8 with bit 4 = h), columns 32vt + 16c16 + 4(s16%4) .. +3; the block
+  // then holds column 32vt + 16c16 + s16 of keys kb+4e .. kb+4e+3.
+  const int s16 = lane & 15, c16 = (lane >> 4) & 1, a = s16 >> 2;
+  const int cc = 2 * c16 + ((s16 >> 1) & 1);
+  o.v = (16 * h + a) * 128 + ((cc ^ (4 * (a >> 1) + h)) << 4) + 8 * (s16 & 1);
+  // Page loads: key i/8 of the group, chunk slot i%8 <- source chunk
+  // (i%8) ^ (4 bit4(i) + 2 bit5(i) + bit1(wave)).
+  o.load = wave * (8 * kRowBytes) + (lane >> 3) * kRowBytes +
+           16 * ((lane & 7) ^ (4 * ((lane >> 4) & 1) + 2 * ((lane >> 5) & 1) + ((wave >> 1) & 1)));
+  return o;
 }
 
 // FP8: the cache holds e4m3 bytes (kv_descale is read); else bf16.
@@ -539,49 +568,11 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
     return;
 
   const int row0 = blockIdx.y * kRowsPerBlock + wave * kRowsPerWave;  // first row of this wave
-  const int r = row0 + n;                                             // this lane's query row
   const bool wave_active = row0 < P.rows;
-  const bool row_valid = r < P.rows;
-  const int i_tok = row_valid ? r / P.heads : 0;
   const int i_tok_min = row0 / P.heads;  // smallest token index among the wave's rows
-
-  // ---- per-lane LDS offsets (relative to a page buffer) -------------------
-  // Page loads: key i/8 of the group, chunk slot i%8 <- source chunk
-  // (i%8) ^ (4 bit4(i) + 2 bit5(i) + bit1(wave)).
-  const uint32_t load_voff0 =
-      wave * (8 * kRowBytes) + (lane >> 3) * kRowBytes +
-      16 * ((lane & 7) ^ (4 * ((lane >> 4) & 1) + 2 * ((lane >> 5) & 1) + ((wave >> 1) & 1)));
-  const uint32_t load_voff1 = load_voff0 + 4 * (8 * kRowBytes);  // key group wave + 4
-  const uint32_t load_voff_f8 = wave * 1024 + 16 * lane;
-  // S^T A operand: lane (m = n, h) reads key 32t + sigma(m) with
-  // sigma(8q + 4g + t') = 16g + 4q + t', global chunk 2ks + h, i.e. column
-  // block ks/4, chunk 2(ks%4) + h of the block.  Keys 32 apart share the
-  // swizzle, so tile 1 is tile 0 plus 32 rows of 128 bytes.
-  const int sig = 16 * ((n >> 2) & 1) + 4 * (n >> 3) + (n & 3);
-  uint32_t koff[4];
-  {
-    const int sw = 4 * ((sig >> 1) & 1) + 2 * ((sig >> 2) & 1) + ((sig >> 4) & 1);
-    const int x = h ^ sw;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) koff[i] = sig * 128 + (((2 * i) ^ x) << 4);
-  }
-  // V^T A operand via ds_read_b64_tr_b16: in the 16-lane block (c16, s16)
-  // of half h, source lane s16 addresses key kb + 4e + s16/4 (kb a multiple
-  // of 8 with bit 4 = h), columns 32vt + 16c16 + 4(s16%4) .. +3; the block
-  // then holds column 32vt + 16c16 + s16 of keys kb+4e .. kb+4e+3.
-  const int s16 = lane & 15;
-  const int c16 = (lane >> 4) & 1;
-  uint32_t voff[2][2];  // [e][vt parity]
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int a = s16 >> 2;
-    const int sw = 4 * (a >> 1) + 2 * e + h;
-#pragma unroll
-    for (int par = 0; par < 2; ++par) {
-      const int cc = 4 * par + 2 * c16 + ((s16 >> 1) & 1);
-      voff[e][par] = (16 * h + 4 * e + a) * 128 + ((cc ^ sw) << 4) + 8 * (s16 & 1);
-    }
-  }
+  // This lane's query row is row0 + n, n = lane % 32.  That and the lane's
+  // LDS offsets are recomputed where used, from a lane id read through pin()
+  // (see lane_offsets), instead of being held across the page loop.
 
   // LDS starts as zeros: a load lane that falls outside a page's range may
   // leave its bytes untouched, and those bytes must be finite.
@@ -608,10 +599,12 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
     if constexpr (FP8)
       issue_loads_f8(std::make_integer_sequence<int, kLoadsPerWaveF8>{},
                      page_rsrc<kD>(kv + nphys * kSrcPageBytes, vr),
-                     smem + kPageBytes + (j & 1) * kPageBytesF8, wave, load_voff_f8);
-    else
+                     smem + kPageBytes + (j & 1) * kPageBytesF8, wave, wave * 1024 + 16 * lane);
+    else {
+      const uint32_t lo = lane_offsets(lane, wave).load;
       issue_page_loads(page_rsrc<kRowBytes>(kv + nphys * kSrcPageBytes, vr),
-                       smem + (j & 1) * kPageBytes, wave, load_voff0, load_voff1);
+                       smem + (j & 1) * kPageBytes, wave, lo, lo + 4 * (8 * kRowBytes));
+    }
   };
   // Move the cursor one page on and read that page's block-table entry and
   // length.  Called after a page's compute, so the scalar loads have a whole
@@ -667,12 +660,13 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
     // ---- one piece: pages [cp, cend) of request cb ---------------------------
     const int32_t L = seq_lens[cb];
     const int cend = (cb == b_last) ? pg_last : page_count(L);
-    const int32_t lim = P.causal ? L - P.q_len + i_tok : L - 1;  // last visible key
     // pages from first_masked on may hold keys some row of this wave cannot see
     const int32_t lim_min = P.causal ? L - P.q_len + i_tok_min : L - 1;
     const int first_masked =
         __builtin_amdgcn_readfirstlane(lim_min >= 0 ? (lim_min + 1) / kPage : 0);
     {
+      const int r = row0 + (pinned_lane() & 31);
+      const bool row_valid = r < P.rows;
       const uint16_t* qrow = q + ((int64_t)cb * P.rows + (row_valid ? r : 0)) * kD + 8 * h;
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
@@ -686,7 +680,14 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
     for (int vt = 0; vt < kVTiles; ++vt) oacc[vt] = (f32x16){};
     float m_run = -INFINITY, l_run = 0.f;
 
-    for (; cp < cend && it < total; ++cp, ++it) {
+    // One page of the piece.  MASKED: some key of the page may be invisible to
+    // some row of the wave (page tail, causal limit); those pages (at most
+    // the last one or, for several tokens per request, the last few) run
+    // one tile at a time with explicit masking.  The two kinds run as two
+    // loops rather than a branch inside one, which keeps the 256 output
+    // registers in place.
+    auto page = [&](auto masked_c) {
+      constexpr bool MASKED = decltype(masked_c)::value;
       __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of page `it` landed
       __syncthreads();                     // ... and every wave's; buffer it+1 is free again
       const lds_u8* base = LDS_PTR(uint8_t, smem) + (FP8 ? 0 : (it & 1) * kPageBytes);
@@ -699,14 +700,16 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
                                            __builtin_amdgcn_readfirstlane(nrows));
       uint8_t* const next_buf = FP8 ? smem + kPageBytes + ((it + 1) & 1) * kPageBytesF8
                                     : smem + ((it + 1) & 1) * kPageBytes;
+      const uint32_t plane = pinned_lane();
+      const LaneOffsets lo = lane_offsets(plane, wave);
       // load K of this wave's share, K < 18 (bf16) or K < 9 (e4m3)
       auto load = [&](auto kc) {
         constexpr int K = decltype(kc)::value;
         if (has_next) {
           if constexpr (FP8)
-            issue_one_load_f8<K>(next_rsrc, next_buf, wave, load_voff_f8);
+            issue_one_load_f8<K>(next_rsrc, next_buf, wave, wave * 1024 + 16 * plane);
           else
-            issue_one_load<K>(next_rsrc, next_buf, wave, load_voff0, load_voff1);
+            issue_one_load<K>(next_rsrc, next_buf, wave, lo.load, lo.load + 4 * (8 * kRowBytes));
         }
       };
       auto hook_s0 = [&](auto g) { load(g); };
@@ -724,88 +727,200 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
 
       // LDS byte addresses of this page's operands
       const uint32_t pbase = (uint32_t)(uintptr_t)base;
-      uint32_t ka[4], ka_hi[4], va[2][2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ka[i] = pbase + koff[i];
-        ka_hi[i] = ka[i] + 32768;
-      }
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-#pragma unroll
-        for (int par = 0; par < 2; ++par) va[e][par] = pbase + voff[e][par];
+      const uint32_t ka = pbase + lo.k, va = pbase + lo.v;
 
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        // ---- S^T = K Q^T for 32-key tile t; sc[i] is key 32t + 16h + i -----------
-        f32x16 sc;
-        if (t == 0)
-          score_tile<0>(sc, ka, ka_hi, qreg, hook_s0);
-        else
-          score_tile<32 * 128>(sc, ka, ka_hi, qreg, hook_s1);
-        // ---- row max of the scaled scores; weights p = 2^(c s - m) -----------------
-        // c = softmax_scale * log2(e) > 0, so max(c s) = c max(s).  Keys a row
-        // cannot see (causal limit, page tail) are excluded on the pages
-        // where they can occur.
-        const int key0 = cp * kPage + 32 * t + 16 * h;
-        const bool masked = cp >= first_masked;
-        float mx[4];
-        if (masked) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            mx[j] = -INFINITY;
-#pragma unroll
-            for (int i = j; i < 16; i += 4)
-              mx[j] = fmaxf(mx[j], (key0 + i <= lim) ? sc[i] : -INFINITY);
+      if constexpr (!MASKED) {
+        // ---- no key of this page is masked for any row of the wave ----------------
+        // The softmax of each tile runs in the shadow of the matrix work:
+        //   S(0)
+        //   S(1)  | max(0), rescale decision (between groups), weights P(0)
+        //   PV(0) | max(1)
+        //   rescale decision, weights P(1) for keys 0..15 of the tile
+        //   PV(1) | weights P(1) for keys 16..31 (used from group 4 on)
+        // sc0[i] / sc1[i] is key 16h + i of tile 0 / 1.
+        f32x16 sc0, sc1;
+        score_tile<0>(sc0, ka, qreg, hook_s0, NoSlot{});
+
+        float mx[4], ls[4];
+        float m_tile = 0.f, neg_m = 0.f;
+        bool need = false;
+        uint32_t pk[8];
+        // row max of tile `sc` in slots 0..4: m_tile, need
+        auto max_slots = [&](const f32x16& sc, auto slot) {
+          constexpr int k = decltype(slot)::value;
+          if constexpr (k < 4) {
+            float x0 = sc[k], x1 = sc[k + 4], x2 = sc[k + 8], x3 = sc[k + 12];
+            pin(x0), pin(x1), pin(x2), pin(x3);
+            mx[k] = fmaxf(fmaxf(x0, x1), fmaxf(x2, x3));
+            pin(mx[k]);
+          } else if constexpr (k == 4) {
+            const float mloc = xhalf_max(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])));
+            m_tile = c_log2 * mloc;
+            pin(m_tile);
           }
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            mx[j] = fmaxf(fmaxf(sc[j], sc[j + 4]), fmaxf(sc[j + 8], sc[j + 12]));
-        }
-        const float mloc = xhalf_max(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])));
-        const float m_tile = (mloc == -INFINITY) ? -INFINITY : c_log2 * mloc;
-        const bool need = m_tile > m_run + kTau;
-        if (__any(need)) {
-          const float m_new = need ? m_tile : m_run;
-          const float alpha = need ? exp2f(m_run - m_new) : 1.0f;
-          l_run *= alpha;
-          // Rows whose running max is still -inf have o = 0: only a wave with
-          // some earlier weight needs the 256-register rescale.
-          if (__any(need && m_run != -INFINITY)) {
-#pragma unroll
-            for (int vt = 0; vt < kVTiles; ++vt) scale_tile(oacc[vt], alpha);
+        };
+        // weight of element i of tile `sc`; pairs are packed to bf16
+        auto weight = [&](const f32x16& sc, auto ii, float (&pf)[2]) {
+          constexpr int i = decltype(ii)::value;
+          float x = sc[i];
+          pin(x);
+          const float pv = __builtin_amdgcn_exp2f(fmaf(x, c_log2, neg_m));
+          ls[i & 3] += pv;
+          pin(ls[i & 3]);
+          pf[i & 1] = pv;
+          if constexpr (i & 1) {
+            pk[i >> 1] = __builtin_bit_cast(uint32_t,
+                                            __builtin_convertvector((f32x2){pf[0], pf[1]}, bf16x2));
+            pin(pk[i >> 1]);
           }
-          m_run = m_new;
-        }
-        const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
+        };
+        // lazy rescale: move the running max only when the tile's max exceeds it by
+        // more than kTau (p <= 2^kTau otherwise); rows still at -inf have o = 0
+        auto decide = [&]() {
+          need = m_tile > m_run + kTau;
+          if (__any(need)) {
+            const float m_new = need ? m_tile : m_run;
+            const float alpha = need ? exp2f(m_run - m_new) : 1.0f;
+            l_run *= alpha;
+            if (__any(need && m_run != -INFINITY)) {
+#pragma unroll
+              for (int vt = 0; vt < kVTiles; ++vt) scale_tile(oacc[vt], alpha);
+            }
+            m_run = m_new;
+          }
+          neg_m = -m_run;  // finite: this tile has a finite max
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ls[j] = 0.f;
+        };
+        float pf[2];
+        auto pay_s1 = [&](auto slot) {
+          constexpr int k = decltype(slot)::value;
+          if constexpr (k <= 4)
+            max_slots(sc0, slot);
+          else if constexpr (k >= 8 && k < 24)
+            weight(sc0, ic<k - 8>{}, pf);
+          else if constexpr (k == 24) {
+            l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+            pin(l_run);
+          }
+        };
+        auto hook_s1f = [&](auto g) {
+          hook_s1(g);
+          if constexpr (decltype(g)::value == 1) decide();
+        };
+        score_tile<32 * 128>(sc1, ka, qreg, hook_s1f, pay_s1);
+
         bf16x8 pop[2];
-        float ls[4] = {0.f, 0.f, 0.f, 0.f};
-        if (masked) {
+        pop[0] = __builtin_bit_cast(bf16x8, (u32x4){pk[0], pk[1], pk[2], pk[3]});
+        pop[1] = __builtin_bit_cast(bf16x8, (u32x4){pk[4], pk[5], pk[6], pk[7]});
+        auto pay_pv0 = [&](auto slot) {
+          if constexpr (decltype(slot)::value <= 4) max_slots(sc1, slot);
+        };
+        pv_tile<0>(oacc, pop, va, hook_pv0, pay_pv0);
+
+        decide();
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float e = __builtin_amdgcn_exp2f(fmaf(sc[i], c_log2, neg_m));
-            const float p = (key0 + i <= lim) ? e : 0.f;
-            ls[i & 3] += p;
-            pop[i >> 3][i & 7] = (__bf16)p;
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(sc[i], c_log2, neg_m));
-            ls[i & 3] += p;
-            pop[i >> 3][i & 7] = (__bf16)p;
-          }
+        for (int i = 0; i < 8; ++i) {
+          const float pv = __builtin_amdgcn_exp2f(fmaf(sc1[i], c_log2, neg_m));
+          ls[i & 3] += pv;
+          pf[i & 1] = pv;
+          if (i & 1)
+            pk[i >> 1] = __builtin_bit_cast(uint32_t,
+                                            __builtin_convertvector((f32x2){pf[0], pf[1]}, bf16x2));
         }
-        l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-        // ---- O^T += V^T P^T ------------------------------------------------------------
-        if (t == 0)
-          pv_tile<0>(oacc, pop, va, hook_pv0);
-        else
-          pv_tile<1>(oacc, pop, va, no_hook);
+        pop[0] = __builtin_bit_cast(bf16x8, (u32x4){pk[0], pk[1], pk[2], pk[3]});
+        auto pay_pv1 = [&](auto slot) {
+          constexpr int k = decltype(slot)::value;
+          if constexpr (k < 8) {
+            weight(sc1, ic<k + 8>{}, pf);
+            if constexpr (k == 7)
+              pop[1] = __builtin_bit_cast(bf16x8, (u32x4){pk[4], pk[5], pk[6], pk[7]});
+          } else if constexpr (k == 8) {
+            l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+            pin(l_run);
+          }
+        };
+        pv_tile<1>(oacc, pop, va, no_hook, pay_pv1);
+      } else {
+        // ---- a page where some key may be masked: one tile at a time --------------
+        const int r = row0 + (plane & 31);
+        const int i_tok = r < P.rows ? r / P.heads : 0;
+        const int32_t lim = P.causal ? L - P.q_len + i_tok : L - 1;  // last visible key
+  #pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          // ---- S^T = K Q^T for 32-key tile t; sc[i] is key 32t + 16h + i -----------
+          f32x16 sc;
+          if (t == 0)
+            score_tile<0>(sc, ka, qreg, hook_s0, NoSlot{});
+          else
+            score_tile<32 * 128>(sc, ka, qreg, hook_s1, NoSlot{});
+          // ---- row max of the scaled scores; weights p = 2^(c s - m) -----------------
+          // c = softmax_scale * log2(e) > 0, so max(c s) = c max(s).  Keys a row
+          // cannot see (causal limit, page tail) are excluded on the pages
+          // where they can occur.
+          const int key0 = cp * kPage + 32 * t + 16 * h;
+          const bool masked = cp >= first_masked;
+          float mx[4];
+          if (masked) {
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              mx[j] = -INFINITY;
+  #pragma unroll
+              for (int i = j; i < 16; i += 4)
+                mx[j] = fmaxf(mx[j], (key0 + i <= lim) ? sc[i] : -INFINITY);
+            }
+          } else {
+  #pragma unroll
+            for (int j = 0; j < 4; ++j)
+              mx[j] = fmaxf(fmaxf(sc[j], sc[j + 4]), fmaxf(sc[j + 8], sc[j + 12]));
+          }
+          const float mloc = xhalf_max(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])));
+          const float m_tile = (mloc == -INFINITY) ? -INFINITY : c_log2 * mloc;
+          const bool need = m_tile > m_run + kTau;
+          if (__any(need)) {
+            const float m_new = need ? m_tile : m_run;
+            const float alpha = need ? exp2f(m_run - m_new) : 1.0f;
+            l_run *= alpha;
+            // Rows whose running max is still -inf have o = 0: only a wave with
+            // some earlier weight needs the 256-register rescale.
+            if (__any(need && m_run != -INFINITY)) {
+  #pragma unroll
+              for (int vt = 0; vt < kVTiles; ++vt) scale_tile(oacc[vt], alpha);
+            }
+            m_run = m_new;
+          }
+          const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
+          bf16x8 pop[2];
+          float ls[4] = {0.f, 0.f, 0.f, 0.f};
+          if (masked) {
+  #pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const float e = __builtin_amdgcn_exp2f(fmaf(sc[i], c_log2, neg_m));
+              const float p = (key0 + i <= lim) ? e : 0.f;
+              ls[i & 3] += p;
+              pop[i >> 3][i & 7] = (__bf16)p;
+            }
+          } else {
+  #pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const float p = __builtin_amdgcn_exp2f(fmaf(sc[i], c_log2, neg_m));
+              ls[i & 3] += p;
+              pop[i >> 3][i & 7] = (__bf16)p;
+            }
+          }
+          l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+          // ---- O^T += V^T P^T ------------------------------------------------------------
+          if (t == 0)
+            pv_tile<0>(oacc, pop, va, hook_pv0, NoSlot{});
+          else
+            pv_tile<1>(oacc, pop, va, no_hook, NoSlot{});
+        }
       }
       if (it + 1 < total) advance();
-    }
+    };
+    const int cfast = min(cend, max(cp, first_masked));
+    for (; cp < cfast && it < total; ++cp, ++it) page(std::false_type{});
+    for (; cp < cend && it < total; ++cp, ++it) page(std::true_type{});
 
     // ---- epilogue of the piece ---------------------------------------------------
     {
@@ -815,7 +930,8 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
           l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
       const int k0 = split_indptr[cb];
       const int k = split_indptr[cb + 1] - k0;
-      if (row_valid) {
+      const int r = row0 + (pinned_lane() & 31);
+      if (r < P.rows) {
         const int64_t slot = (int64_t)k0 + piece;
         if (k > 1 && slot < P.partial_slots) {
           float* dst = partial_o + (slot * P.rows + r) * kDv + 4 * h;

@@ -1,0 +1,122 @@
+"""Guard on the decode kernel's generated code (CPU only: compiles to gfx950
+assembly with the library's flags, reads no GPU).
+
+The kernel issues LDS operand reads from inline assembly and waits for them
+with separate statements (s_waitcnt lgkmcnt(N)), so the compiler does not
+know those registers are being written in the background.  This test walks
+each kernel's instruction stream and checks that no instruction touches a
+register of a read that is still in flight: LDS reads complete in order, so
+after lgkmcnt(N) every LDS read except the newest N has landed.
+"""
+
+import os
+import re
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+from paged_kv_mla_req_amd import build as B
+
+HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+
+_REG = re.compile(r"(?<![\w.])([vas])(?:\[(\d+):(\d+)\]|(\d+))(?![\w])")
+
+
+def _regs(text):
+    out = set()
+    for kind, lo, hi, one in _REG.findall(text):
+        if one:
+            out.add((kind, int(one)))
+        else:
+            out.update((kind, r) for r in range(int(lo), int(hi) + 1))
+    return out
+
+
+def _kernels(asm: str):
+    """name -> list of instruction lines, for each mla_decode_kernel body."""
+    bodies, cur, name = {}, None, None
+    for line in asm.splitlines():
+        m = re.match(r"^(_Z\S*mla_decode_kernel\S*):", line)
+        if m:
+            name, cur = m.group(1), []
+            continue
+        if cur is None:
+            continue
+        s = line.split(";")[0].strip()
+        if s.startswith(".Lfunc_end") or s == "s_endpgm":
+            bodies[name], cur = cur, None
+            continue
+        if not s or s.endswith(":") or s.startswith("."):
+            continue
+        cur.append(s)
+    return bodies
+
+
+def _check(instrs):
+    inflight = []  # destination register sets of LDS reads, oldest first
+    bad = []
+    for i, ins in enumerate(instrs):
+        op = ins.split()[0]
+        if op == "s_waitcnt":
+            m = re.search(r"lgkmcnt\((\d+)\)", ins)
+            if m:
+                n = int(m.group(1))
+                inflight = inflight[len(inflight) - n:] if n < len(inflight) else inflight
+            continue
+        if op in ("s_nop", "s_barrier"):
+            continue
+        busy = set().union(*inflight) if inflight else set()
+        operands = ins[len(op):]
+        if op.startswith("ds_read") or op.startswith("ds_bpermute"):
+            dst, _, rest = operands.partition(",")
+            if busy & _regs(operands):
+                bad.append((i, ins))
+            inflight.append(_regs(dst))
+            continue
+        if op.startswith("ds_"):
+            if busy & _regs(operands):
+                bad.append((i, ins))
+            inflight.append(set())  # counts in lgkmcnt, writes no register
+            continue
+        if busy & _regs(operands):
+            bad.append((i, ins))
+    return bad
+
+
+@pytest.fixture(scope="module")
+def decode_asm():
+    if not os.path.exists(HIPCC):
+        pytest.skip("hipcc not available")
+    with tempfile.TemporaryDirectory() as d:
+        out = os.path.join(d, "decode.s")
+        flags = [f for f in B.COMMON_FLAGS if f not in ("-fPIC",)]
+        cmd = [HIPCC, *flags, *B.SOURCE_FLAGS.get("decode.hip", []), "--cuda-device-only", "-S",
+               os.path.join(B.CSRC, "decode.hip"), "-o", out]
+        subprocess.run(cmd, check=True, capture_output=True, timeout=600)
+        with open(out) as f:
+            return f.read()
+
+
+def test_both_kernels_present(decode_asm):
+    names = list(_kernels(decode_asm))
+    assert len(names) == 2, names
+
+
+def test_no_instruction_touches_an_in_flight_lds_read(decode_asm):
+    for name, instrs in _kernels(decode_asm).items():
+        bad = _check(instrs)
+        assert not bad, f"{name}: {len(bad)} instructions touch in-flight registers, e.g. {bad[:5]}"
+
+
+def test_checker_flags_a_planted_use():
+    """The walk itself: a use of a read's register before its wait is found,
+    the same use after the wait is not."""
+    good = ["ds_read_b128 v[4:7], v1", "s_waitcnt lgkmcnt(0)", "v_add_f32_e32 v8, v4, v5"]
+    bad = ["ds_read_b128 v[4:7], v1", "v_add_f32_e32 v8, v4, v5", "s_waitcnt lgkmcnt(0)"]
+    partial = ["ds_read_b128 v[4:7], v1", "ds_read_b128 v[8:11], v1", "s_waitcnt lgkmcnt(1)",
+               "v_mov_b32_e32 v0, v5", "v_mov_b32_e32 v0, v9"]
+    assert _check(good) == []
+    assert len(_check(bad)) == 1
+    assert [i for i, _ in _check(partial)] == [4]
