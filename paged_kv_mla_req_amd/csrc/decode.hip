@@ -538,6 +538,62 @@ __device__ __forceinline__ LaneOffsets lane_offsets(uint32_t lane, int wave) {
   return o;
 }
 
+// Bytes of LDS each wave has for staging its output rows (outside the page
+// buffers, so no other wave is ever waiting on them).
+constexpr int kStageBytes = 4096;
+
+// Write this wave's 32 rows of o * scale, as rows of 512 values, to dst
+// (row r of the request at dst + r * 512; rows >= rows are skipped), in
+// bf16 (T = uint16_t) or fp32 (T = float).  The accumulators hold O^T
+// (lane (n, h): row n, 16 values per tile), so direct stores would write
+// 8- or 16-byte pieces of 32 rows per instruction.  Instead the rows pass
+// through the wave's own LDS area, 128 bytes of each row at a time (the
+// 16-byte chunk c of row n sits at c ^ (n % 8), which spreads both the
+// writes and the reads over the banks), and leave as whole 128-byte row
+// segments, 8 rows per store instruction.
+template <typename T>
+__device__ __forceinline__ void store_rows(const f32x16 (&oacc)[kVTiles], float scale,
+                                           uint8_t* stage, T* dst, int row0, int rows,
+                                           uint32_t lane) {
+  constexpr bool kBf16 = sizeof(T) == 2;
+  constexpr int kTiles = kBf16 ? 2 : 1;  // accumulator tiles per 128-byte row segment
+  constexpr int kCols = 32 * kTiles;     // columns per pass
+  const int n = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int p = 0; p < kVTiles / kTiles; ++p) {
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        // this lane's 4 values: columns 32 (kTiles p + t) + 8 g + 4 h .. +3
+        const f32x16& o = oacc[kTiles * p + t];
+        const float v0 = o[4 * g] * scale, v1 = o[4 * g + 1] * scale;
+        const float v2 = o[4 * g + 2] * scale, v3 = o[4 * g + 3] * scale;
+        if constexpr (kBf16) {
+          const int c = 4 * t + g;  // 16-byte chunk (8 columns); this lane has half
+          const uint32_t lo =
+              __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){v0, v1}, bf16x2));
+          const uint32_t hi =
+              __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){v2, v3}, bf16x2));
+          *reinterpret_cast<uint2*>(stage + n * 128 + ((c ^ (n & 7)) << 4) + 8 * h) =
+              make_uint2(lo, hi);
+        } else {
+          const int c = 2 * g + h;  // 16-byte chunk (4 columns), all this lane's
+          *reinterpret_cast<float4*>(stage + n * 128 + ((c ^ (n & 7)) << 4)) =
+              make_float4(v0, v1, v2, v3);
+        }
+      }
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int row = 8 * qq + (int)(lane >> 3), j = lane & 7;
+      const uint4 v = *reinterpret_cast<const uint4*>(stage + row * 128 + ((j ^ (row & 7)) << 4));
+      if (row0 + row < rows)
+        *reinterpret_cast<uint4*>(dst + (int64_t)(row0 + row) * kDv + kCols * p +
+                                  j * (16 / (int)sizeof(T))) = v;
+    }
+  }
+}
+
 // FP8: the cache holds e4m3 bytes (kv_descale is read); else bf16.
 template <bool FP8>
 __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -550,6 +606,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
   // bf16: two compute buffers.  fp8: compute buffer 0, and two e4m3 staging
   // buffers in the space of compute buffer 1.
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kPageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t stage_all[kWaves][kStageBytes];
   constexpr int kSrcPageBytes = FP8 ? kPageBytesF8 : kPageBytes;
 
   const int lane = threadIdx.x & 63;
@@ -930,35 +987,18 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
           l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
       const int k0 = split_indptr[cb];
       const int k = split_indptr[cb + 1] - k0;
-      const int r = row0 + (pinned_lane() & 31);
-      if (r < P.rows) {
-        const int64_t slot = (int64_t)k0 + piece;
-        if (k > 1 && slot < P.partial_slots) {
-          float* dst = partial_o + (slot * P.rows + r) * kDv + 4 * h;
-#pragma unroll
-          for (int vt = 0; vt < kVTiles; ++vt)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              float4 v = make_float4(oacc[vt][4 * g] * inv, oacc[vt][4 * g + 1] * inv,
-                                     oacc[vt][4 * g + 2] * inv, oacc[vt][4 * g + 3] * inv);
-              *reinterpret_cast<float4*>(dst + 32 * vt + 8 * g) = v;
-            }
-          if (h == 0) partial_lse[slot * P.rows + r] = lse_val;
-        } else if (k <= 1) {
-          uint16_t* dst = out + ((int64_t)cb * P.rows + r) * kDv + 4 * h;
-#pragma unroll
-          for (int vt = 0; vt < kVTiles; ++vt)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              uint2 v;
-              v.x = (uint32_t)f32_to_bf16(oacc[vt][4 * g] * inv) |
-                    ((uint32_t)f32_to_bf16(oacc[vt][4 * g + 1] * inv) << 16);
-              v.y = (uint32_t)f32_to_bf16(oacc[vt][4 * g + 2] * inv) |
-                    ((uint32_t)f32_to_bf16(oacc[vt][4 * g + 3] * inv) << 16);
-              *reinterpret_cast<uint2*>(dst + 32 * vt + 8 * g) = v;
-            }
-          if (lse_out && h == 0) lse_out[(int64_t)cb * P.rows + r] = lse_val;
-        }
+      const int64_t slot = (int64_t)k0 + piece;
+      // A piece of a split request goes to its partial slot (normalised o and
+      // lse, fp32); the only piece of a request is final (bf16 o).
+      const bool to_partial = k > 1;
+      const uint32_t ln = pinned_lane();
+      const int r = row0 + (int)(ln & 31);
+      if (to_partial && slot < P.partial_slots) {
+        if ((ln >> 5) == 0 && r < P.rows) partial_lse[slot * P.rows + r] = lse_val;
+        store_rows(oacc, inv, stage_all[wave], partial_o + slot * P.rows * kDv, row0, P.rows, ln);
+      } else if (!to_partial) {
+        if (lse_out && (ln >> 5) == 0 && r < P.rows) lse_out[(int64_t)cb * P.rows + r] = lse_val;
+        store_rows(oacc, inv, stage_all[wave], out + (int64_t)cb * P.rows * kDv, row0, P.rows, ln);
       }
     }
     if (it >= total || cb >= b_last) break;
@@ -1036,13 +1076,14 @@ extern "C" mla_status mla_decode(const void* q, int32_t bs, int32_t q_len, int32
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(q);
     const uint8_t* kvp = reinterpret_cast<const uint8_t*>(kv_cache);
     uint16_t* op = reinterpret_cast<uint16_t*>(out);
+    float* po = partial_o;
     if (ev_start || ev_stop)
       hipExtLaunchKernelGGL(kernel, grid, dim3(kWaves * 64), 0, stream, ev_start, ev_stop, 0, qp,
                             kvp, block_table, seq_lens, tile_plan, split_indptr, descale,
-                            partial_o, partial_lse, op, lse, p);
+                            po, partial_lse, op, lse, p);
     else
       hipLaunchKernelGGL(kernel, grid, dim3(kWaves * 64), 0, stream, qp, kvp, block_table,
-                         seq_lens, tile_plan, split_indptr, descale, partial_o, partial_lse, op,
+                         seq_lens, tile_plan, split_indptr, descale, po, partial_lse, op,
                          lse, p);
   };
   if (kv_dtype == MLA_KV_FP8_E4M3)
