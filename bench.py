@@ -38,6 +38,8 @@ def _args():
                     help="independent copies of the KV pool, rotated per step so that the "
                          "256 MB last-level cache cannot serve a step from the previous one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eagerly launched steps instead of replays of a captured HIP graph")
     ap.add_argument("--cpu-runs", type=int, default=3)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before warm-up, run one plain elementwise kernel (bitwise not) that "
@@ -239,14 +241,40 @@ def main() -> int:
     for i in range(a.warmup):
         step(i, -1)
     torch.cuda.synchronize()
-    print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
+    graphs = []
+    if not a.eager:
+        # One captured step per KV pool: the four kernels of the step replay
+        # without host launch work between them.
+        for j in range(len(pools)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(j, -1)
+            graphs.append(g)
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+
+    print(f"[bench] timing {a.steps} steps ({'eager' if a.eager else 'graph replays'})",
+          file=sys.stderr, flush=True)
     t0 = time.perf_counter()
     for i in range(a.steps):
-        step(a.warmup + i, i)
+        if graphs:
+            graphs[i % len(graphs)].replay()
+        else:
+            step(a.warmup + i, i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / a.steps
-    # the decode kernel's average launch duration over the timed steps
+    ms_step_eager = None
+    if graphs:
+        # The decode kernel's own duration comes from eager steps (the launch
+        # records the events itself, which a graph replay cannot do).
+        t1 = time.perf_counter()
+        for i in range(a.steps):
+            step(a.warmup + i, i)
+        torch.cuda.synchronize()
+        ms_step_eager = (time.perf_counter() - t1) * 1e3 / a.steps
+    # the decode kernel's average launch duration over the event-timed steps
     dec_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
 
     b = _algorithmic_bytes(w)
@@ -281,6 +309,8 @@ def main() -> int:
         "pct_hbm_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(tokens_s, 1),
         "decode_kernel_ms": round(dec_ms, 5),
+        "step_launch": "eager" if a.eager else "hip graph replay",
+        "ms_per_step_eager": None if ms_step_eager is None else round(ms_step_eager, 5),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),

@@ -110,13 +110,15 @@ mla_status mla_build_block_table(const int32_t* req_to_token, int32_t r2t_rows,
  * work-groups (the get_mla_metadata call of init_forward_metadata: a
  * [num_parts, 8] table and a bs+1 vector; num_parts at most the CU count).
  *
- * Rule (deterministic, depends only on seq_lens, rows_per_req, num_parts):
- * request b has N_b = ceil(L_b/64) pages and costs N_b + c page units, with
- * c = 1 + rows_per_req/64 (0 for an empty request).  With C the total cost,
- * part p covers cost positions [floor(pC/P), floor((p+1)C/P)); a position x
- * inside request b maps to the page boundary clamp(x - cum_b - c, 0, N_b).
- * Each part therefore costs at most ceil(C/P) + c units, every page lies in
- * exactly one part, and the number of pieces is at most bs + num_parts.
+ * Rule (deterministic, depends only on seq_lens, rows_per_req, num_parts),
+ * in quarter pages: request b has N_b = ceil(L_b/64) pages and costs
+ * 4 N_b + c, with c = 4 + ceil(10 rows_per_req / 128) the per-piece overhead
+ * (0 for an empty request).  With C the total cost, part p covers cost
+ * positions [floor(pC/P), floor((p+1)C/P)); a position x inside request b
+ * maps to the page boundary clamp(floor((x - cum_b - c + 2) / 4), 0, N_b).
+ * Each part therefore costs at most ceil(C/P) + c + 4 units (counting c for
+ * every piece it holds), every page lies in exactly one part, and the number
+ * of pieces is at most bs + num_parts.
  *
  *   tile_plan     int32 [num_parts, 8]: begin_req, begin_page, end_req
  *                 (inclusive), end_page (exclusive, in end_req), piece index

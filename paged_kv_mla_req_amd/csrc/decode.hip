@@ -142,6 +142,13 @@ __device__ __forceinline__ void issue_page_loads(__amdgpu_buffer_rsrc_t rsrc, ui
   issue_loads(std::make_integer_sequence<int, kLoadsPerWave>{}, rsrc, buf, wave, voff0, voff1);
 }
 
+// The lane's index in its wave, from the execution mask (two VALU
+// instructions), so that no register has to carry the work-item id through
+// the kernel.
+__device__ __forceinline__ uint32_t lane_id() {
+  return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
 // e4m3 page: a plain copy into a 36 KiB staging buffer.  Load k of wave w
 // fills staging bytes [1024 j, 1024 j + 1024) with j = w + 4k from the same
 // page offsets; voff = 1024 w + 16 lane.
@@ -172,11 +179,12 @@ __device__ __forceinline__ int chunk_swz(int k) {
 // m = 0..8, i.e. the chunk pair 2 (t % 4), 2 (t % 4) + 1 of column block m.
 // The conversion is exact.  All addresses are a per-thread base plus a
 // constant, so nothing is kept per m.
-__device__ __forceinline__ void convert_f8_page(const uint8_t* stage, uint8_t* buf) {
-  const int key = threadIdx.x >> 2;
-  const int c0 = 2 * (threadIdx.x & 3);
+__device__ __forceinline__ void convert_f8_page(const uint8_t* stage, uint8_t* buf, int wave) {
+  const int tid = wave * 64 + (int)lane_id();
+  const int key = tid >> 2;
+  const int c0 = 2 * (tid & 3);
   const int slot0 = c0 ^ chunk_swz(key);
-  const uint8_t* src = stage + key * kD + 16 * (threadIdx.x & 3);
+  const uint8_t* src = stage + key * kD + 16 * (tid & 3);
   uint8_t* dst0 = buf + key * 128 + (slot0 << 4);
   uint8_t* dst1 = buf + key * 128 + ((slot0 ^ 1) << 4);
 #pragma unroll
@@ -509,7 +517,7 @@ struct LaneOffsets {
 };
 
 __device__ __forceinline__ uint32_t pinned_lane() {
-  uint32_t l = threadIdx.x & 63;
+  uint32_t l = lane_id();
   pin(l);
   return l;
 }
@@ -609,10 +617,8 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
   __shared__ __attribute__((aligned(16))) uint8_t stage_all[kWaves][kStageBytes];
   constexpr int kSrcPageBytes = FP8 ? kPageBytesF8 : kPageBytes;
 
-  const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
-  const int n = lane & 31;      // query row within the wave (B/C column)
-  const int h = lane >> 5;      // lane half
+  const int lane = (int)lane_id();  // used before the page loops only
   const int part = blockIdx.x;
 
   const int32_t* tp = tile_plan + part * 8;
@@ -633,7 +639,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
 
   // LDS starts as zeros: a load lane that falls outside a page's range may
   // leave its bytes untouched, and those bytes must be finite.
-  for (int i = threadIdx.x; i < 2 * kPageBytes / 16; i += kWaves * 64)
+  for (int i = wave * 64 + lane; i < 2 * kPageBytes / 16; i += kWaves * 64)
     reinterpret_cast<u32x4*>(smem)[i] = (u32x4){0, 0, 0, 0};
   __syncthreads();
 
@@ -694,7 +700,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
         advance();
       }
       if constexpr (FP8) {
-        convert_f8_page(smem + kPageBytes + (it & 1) * kPageBytesF8, smem);
+        convert_f8_page(smem + kPageBytes + (it & 1) * kPageBytesF8, smem, wave);
         __syncthreads();
       }
     }
@@ -722,9 +728,11 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
     const int first_masked =
         __builtin_amdgcn_readfirstlane(lim_min >= 0 ? (lim_min + 1) / kPage : 0);
     {
-      const int r = row0 + (pinned_lane() & 31);
+      const uint32_t ql = pinned_lane();
+      const int r = row0 + (int)(ql & 31);
       const bool row_valid = r < P.rows;
-      const uint16_t* qrow = q + ((int64_t)cb * P.rows + (row_valid ? r : 0)) * kD + 8 * h;
+      const uint16_t* qrow =
+          q + ((int64_t)cb * P.rows + (row_valid ? r : 0)) * kD + 8 * (int)(ql >> 5);
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
         u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 16 * ks);
@@ -778,7 +786,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
       };
       auto no_hook = [](auto) {};
       if constexpr (FP8) {
-        convert_f8_page(smem + kPageBytes + (it & 1) * kPageBytesF8, smem);
+        convert_f8_page(smem + kPageBytes + (it & 1) * kPageBytesF8, smem, wave);
         __syncthreads();  // the compute page is complete
       }
 
@@ -915,7 +923,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
           // c = softmax_scale * log2(e) > 0, so max(c s) = c max(s).  Keys a row
           // cannot see (causal limit, page tail) are excluded on the pages
           // where they can occur.
-          const int key0 = cp * kPage + 32 * t + 16 * h;
+          const int key0 = cp * kPage + 32 * t + 16 * (int)(plane >> 5);
           const bool masked = cp >= first_masked;
           float mx[4];
           if (masked) {

@@ -7,14 +7,27 @@
 // does the k-way form for every request whose keys mla_decode split into k
 // pieces:  LSE = M + ln sum_k exp(lse_k - M),  o = sum_k exp(lse_k - LSE) o_k.
 //
-// One wave per (request, row): each lane owns 8 of the 512 value columns
-// (two 16-byte loads per piece), so a piece's row is read fully coalesced.
-// Pure HBM streaming; no MFMA.
+// One wave per (request, row): the lanes first take one piece's lse each
+// (wave max and sum), then each lane owns 8 of the 512 value columns (two
+// 16-byte loads per piece, so a piece's row is read fully coalesced), with
+// the rows of four pieces in flight at a time.  Pure HBM streaming; no MFMA.
 #include "common.h"
 
 namespace mla {
 
 constexpr int kMergeWaves = 4;
+constexpr int kMergeBatch = 4;  // pieces whose rows are loaded together
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x = fmaxf(x, __shfl_xor(x, d, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
+  return x;
+}
 
 __global__ void __launch_bounds__(64 * kMergeWaves)
 merge_states_kernel(const float* __restrict__ partial_o, const float* __restrict__ partial_lse,
@@ -32,24 +45,42 @@ merge_states_kernel(const float* __restrict__ partial_o, const float* __restrict
   float4 acc0 = make_float4(0.f, 0.f, 0.f, 0.f), acc1 = acc0;
   float LSE = -INFINITY;
   if (k > 1) {
-    float M = -INFINITY;
-    for (int s = 0; s < k; ++s) M = fmaxf(M, partial_lse[(int64_t)(k0 + s) * rows + r]);
+    // M and the sum of exp(lse - M): the lanes take the pieces' lse values
+    float m = -INFINITY;
+    for (int s = lane; s < k; s += 64) m = fmaxf(m, partial_lse[(int64_t)(k0 + s) * rows + r]);
+    const float M = wave_max(m);
     if (M != -INFINITY) {
-      float tot = 0.f;
-      for (int s = 0; s < k; ++s) {
-        float l = partial_lse[(int64_t)(k0 + s) * rows + r];
-        tot += (l == -INFINITY) ? 0.f : __expf(l - M);
+      float t = 0.f;
+      for (int s = lane; s < k; s += 64) {
+        const float l = partial_lse[(int64_t)(k0 + s) * rows + r];
+        t += (l == -INFINITY) ? 0.f : __expf(l - M);
       }
-      LSE = M + __logf(tot);
-      for (int s = 0; s < k; ++s) {
-        float l = partial_lse[(int64_t)(k0 + s) * rows + r];
-        if (l == -INFINITY) continue;
-        const float w = __expf(l - LSE);
-        const float4* src = reinterpret_cast<const float4*>(
-            partial_o + ((int64_t)(k0 + s) * rows + r) * kDv) + lane * 2;
-        float4 x0 = src[0], x1 = src[1];
-        acc0.x += w * x0.x; acc0.y += w * x0.y; acc0.z += w * x0.z; acc0.w += w * x0.w;
-        acc1.x += w * x1.x; acc1.y += w * x1.y; acc1.z += w * x1.z; acc1.w += w * x1.w;
+      LSE = M + __logf(wave_sum(t));
+      // o = sum_k exp(lse_k - LSE) o_k, kMergeBatch rows in flight at a time
+      for (int s0 = 0; s0 < k; s0 += kMergeBatch) {
+        float4 x0[kMergeBatch], x1[kMergeBatch];
+        float w[kMergeBatch];
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) {
+          const int s = s0 + j;
+          w[j] = 0.f;
+          x0[j] = x1[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (s < k) {
+            const float l = partial_lse[(int64_t)(k0 + s) * rows + r];
+            w[j] = (l == -INFINITY) ? 0.f : __expf(l - LSE);
+            const float4* src = reinterpret_cast<const float4*>(
+                                    partial_o + ((int64_t)(k0 + s) * rows + r) * kDv) + lane * 2;
+            x0[j] = src[0];
+            x1[j] = src[1];
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) {
+          acc0.x += w[j] * x0[j].x; acc0.y += w[j] * x0[j].y;
+          acc0.z += w[j] * x0[j].z; acc0.w += w[j] * x0[j].w;
+          acc1.x += w[j] * x1[j].x; acc1.y += w[j] * x1[j].y;
+          acc1.z += w[j] * x1[j].z; acc1.w += w[j] * x1[j].w;
+        }
       }
     }
   }

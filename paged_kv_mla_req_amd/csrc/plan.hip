@@ -4,50 +4,55 @@
 // The FlashMLA backend calls get_mla_metadata once per batch step (decode
 // and target-verify) and gets a [num_sm_parts, 8] tile table plus a bs+1
 // split vector; only those shapes are on the page.  The rule below is this
-// library's own (documented in mla_decode.h): request b costs N_b + c page
-// units, part p covers cost positions [floor(pC/P), floor((p+1)C/P)), and a
-// position maps to a page boundary by dropping the first c units of each
-// request.  Everything runs in one work-group: prefix sums over requests,
-// one thread per cut, binary searches for the rest.  Deterministic.
+// library's own (documented in mla_decode.h): in quarter pages, request b
+// costs 4 N_b + c (c: the per-piece overhead of plan_overhead_q), part p
+// covers cost positions [floor(pC/P), floor((p+1)C/P)), and a position maps
+// to the nearest page boundary after dropping the first c units of its
+// request.  One work-group does everything: prefix sums over requests,
+// binary searches for the rest.  Deterministic.
 #include "common.h"
 
 namespace mla {
 
-constexpr int kPlanThreads = 1024;
+// Per-piece overhead in quarter pages: loading q and writing the result of
+// rows_per_req rows, plus a constant (one page of the work costs 4).  On
+// MI355X a 128-row piece costs about 3.4 pages (measured); the rule gives 3.5.
+__host__ __device__ __forceinline__ int plan_overhead_q(int rows_per_req) {
+  return 4 + (10 * rows_per_req + 127) / 128;
+}
 
-// Exclusive prefix sum of one int per thread over the whole block; returns
-// this thread's prefix and writes the block total to *total.
-__device__ int block_exclusive_scan(int v, int* wave_tot, int* total) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+constexpr int kPlanThreads = 256;
+constexpr int kPlanWaves = kPlanThreads / 64;
+
+// Work-group-wide exclusive prefix sum of one int per thread; *total gets
+// the sum.  wave_tot: kPlanWaves ints of LDS.  Two barriers.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int inc = v;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    int t = __shfl_up(inc, d, 64);
+    const int t = __shfl_up(inc, d, 64);
     if (lane >= d) inc += t;
   }
   if (lane == 63) wave_tot[wave] = inc;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int w = 0; w < kPlanThreads / 64; ++w) {
-      int t = wave_tot[w];
-      wave_tot[w] = run;
-      run += t;
-    }
-    *total = run;
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kPlanWaves; ++w) {
+    const int t = wave_tot[w];
+    before += w < wave ? t : 0;
+    all += t;
   }
-  __syncthreads();
-  int res = inc - v + wave_tot[wave];
-  __syncthreads();
-  return res;
+  __syncthreads();  // wave_tot may be reused by the next scan
+  *total = all;
+  return before + inc - v;
 }
 
 // First index i in [0, n) with a[i] > x (n if none).
 __device__ __forceinline__ int upper_bound(const int* a, int n, int x) {
   int lo = 0, hi = n;
   while (lo < hi) {
-    int mid = (lo + hi) >> 1;
+    const int mid = (lo + hi) >> 1;
     if (a[mid] > x) hi = mid; else lo = mid + 1;
   }
   return lo;
@@ -57,120 +62,135 @@ __device__ __forceinline__ int upper_bound(const int* a, int n, int x) {
 __device__ __forceinline__ int lower_bound(const int* a, int n, int x) {
   int lo = 0, hi = n;
   while (lo < hi) {
-    int mid = (lo + hi) >> 1;
+    const int mid = (lo + hi) >> 1;
     if (a[mid] >= x) hi = mid; else lo = mid + 1;
   }
   return lo;
 }
 
+// One work-group of 4 waves: each thread takes a contiguous chunk of the
+// requests (and of the cuts), prefix sums are block scans, lookups are
+// binary searches in LDS.
 __global__ void __launch_bounds__(kPlanThreads)
 plan_splits_kernel(const int32_t* __restrict__ seq_lens, int bs, int overhead, int parts,
                    int32_t* __restrict__ tile_plan, int32_t* __restrict__ split_indptr) {
   extern __shared__ int smem[];
-  int* cum = smem;                    // [bs + 1] cost prefix
+  int* cum = smem;                    // [bs + 1] cost prefix (quarter pages)
   int* pagecum = cum + (bs + 1);      // [bs + 1] page prefix
   int* cuts = pagecum + (bs + 1);     // [parts + 1] flattened page of each cut
   int* fcum = cuts + (parts + 1);     // [parts + 2] prefix count of distinct interior cuts
-  int* wave_tot = fcum + (parts + 2); // [16]
-  int* totals = wave_tot + 16;        // [4]
+  int* wave_tot = fcum + (parts + 2); // [kPlanWaves]
 
   const int t = threadIdx.x;
   const int chunk = (bs + kPlanThreads - 1) / kPlanThreads;
   const int b_begin = min(bs, t * chunk);
   const int b_end = min(bs, b_begin + chunk);
 
-  // 1. prefix sums of cost and pages
+  // 1. prefix sums of cost and pages (pages per request parked in pagecum)
   int my_cost = 0, my_pages = 0;
   for (int b = b_begin; b < b_end; ++b) {
-    int L = seq_lens[b];
-    int n = L > 0 ? (L + kPage - 1) / kPage : 0;
+    const int L = seq_lens[b];
+    const int n = L > 0 ? (L + kPage - 1) / kPage : 0;
+    pagecum[b] = n;
     my_pages += n;
-    my_cost += n > 0 ? n + overhead : 0;
+    my_cost += n > 0 ? 4 * n + overhead : 0;
   }
-  int cost_off = block_exclusive_scan(my_cost, wave_tot, &totals[0]);
-  int page_off = block_exclusive_scan(my_pages, wave_tot, &totals[1]);
+  int C, total_pages;
+  int cost_off = block_exclusive_scan(my_cost, wave_tot, &C);
+  int page_off = block_exclusive_scan(my_pages, wave_tot, &total_pages);
   for (int b = b_begin; b < b_end; ++b) {
-    int L = seq_lens[b];
-    int n = L > 0 ? (L + kPage - 1) / kPage : 0;
+    const int n = pagecum[b];
     cum[b] = cost_off;
     pagecum[b] = page_off;
     page_off += n;
-    cost_off += n > 0 ? n + overhead : 0;
+    cost_off += n > 0 ? 4 * n + overhead : 0;
   }
   if (t == 0) {
-    cum[bs] = totals[0];
-    pagecum[bs] = totals[1];
+    cum[bs] = C;
+    pagecum[bs] = total_pages;
   }
   __syncthreads();
-  const int C = cum[bs];
-  const int total_pages = pagecum[bs];
 
-  // 2. cut positions -> flattened page boundaries
-  if (t <= parts) {
+  // 2. cut positions -> flattened page boundaries (nearest page boundary,
+  //    the first `overhead` units of a request mapping to its page 0)
+  for (int p = t; p <= parts; p += kPlanThreads) {
     int g;
-    const int64_t x = (int64_t)t * C / parts;
-    if (t == parts || x >= C) {
+    const int64_t x = (int64_t)p * C / parts;
+    if (p == parts || x >= C) {
       g = total_pages;
     } else {
-      int b = upper_bound(cum, bs, (int)x) - 1;
-      int o = (int)x - cum[b];
-      int n = pagecum[b + 1] - pagecum[b];
-      g = pagecum[b] + min(max(o - overhead, 0), n);
+      const int b = upper_bound(cum, bs, (int)x) - 1;
+      const int o = (int)x - cum[b];
+      const int n = pagecum[b + 1] - pagecum[b];
+      g = pagecum[b] + min(max(o - overhead + 2, 0) >> 2, n);
     }
-    cuts[t] = g;
+    cuts[p] = g;
   }
   __syncthreads();
 
   // 3. distinct interior cuts (strictly inside a request), prefix-counted
-  int flag = 0;
-  if (t >= 1 && t < parts) {
-    int g = cuts[t];
-    if (g > 0 && g < total_pages && g != cuts[t - 1]) {
-      int b = upper_bound(pagecum, bs, g) - 1;
-      flag = (g - pagecum[b]) > 0;
-    }
+  const int pchunk = (parts + 1 + kPlanThreads - 1) / kPlanThreads;
+  const int p_begin = min(parts + 1, t * pchunk);
+  const int p_end = min(parts + 1, p_begin + pchunk);
+  auto interior = [&](int p) -> int {
+    if (p < 1 || p >= parts) return 0;
+    const int g = cuts[p];
+    if (g <= 0 || g >= total_pages || g == cuts[p - 1]) return 0;
+    const int b = upper_bound(pagecum, bs, g) - 1;
+    return (g - pagecum[b]) > 0;
+  };
+  int flags[4] = {0, 0, 0, 0};  // pchunk <= 3 for parts <= 512
+  int my_flags = 0;
+  for (int p = p_begin; p < p_end; ++p) {
+    const int f = interior(p);
+    if (p - p_begin < 4) flags[p - p_begin] = f;
+    my_flags += f;
   }
-  int fpre = block_exclusive_scan(t <= parts ? flag : 0, wave_tot, &totals[2]);
-  if (t <= parts) fcum[t] = fpre;
-  if (t == 0) fcum[parts + 1] = totals[2];
+  int n_interior;
+  int fpre = block_exclusive_scan(my_flags, wave_tot, &n_interior);
+  for (int p = p_begin; p < p_end; ++p) {
+    fcum[p] = fpre;
+    fpre += (p - p_begin < 4) ? flags[p - p_begin] : interior(p);
+  }
+  if (t == 0) fcum[parts + 1] = n_interior;
   __syncthreads();
 
   // 4. pieces per request -> split_indptr
+  auto pieces_of = [&](int b) -> int {
+    const int lo = pagecum[b], hi = pagecum[b + 1];
+    if (hi == lo) return 0;
+    const int i_lo = upper_bound(cuts, parts + 1, lo);
+    const int i_hi = lower_bound(cuts, parts + 1, hi);
+    return 1 + (i_hi > i_lo ? fcum[i_hi] - fcum[i_lo] : 0);
+  };
   int my_pieces = 0;
-  for (int b = b_begin; b < b_end; ++b) {
-    int lo = pagecum[b], hi = pagecum[b + 1];
-    if (hi == lo) continue;
-    int i_lo = upper_bound(cuts, parts + 1, lo);
-    int i_hi = lower_bound(cuts, parts + 1, hi);
-    my_pieces += 1 + (i_hi > i_lo ? fcum[i_hi] - fcum[i_lo] : 0);
-  }
-  int piece_off = block_exclusive_scan(my_pieces, wave_tot, &totals[3]);
+  for (int b = b_begin; b < b_end; ++b) my_pieces += pieces_of(b);
+  int n_pieces;
+  int piece_off = block_exclusive_scan(my_pieces, wave_tot, &n_pieces);
   for (int b = b_begin; b < b_end; ++b) {
     split_indptr[b] = piece_off;
-    int lo = pagecum[b], hi = pagecum[b + 1];
-    if (hi == lo) continue;
-    int i_lo = upper_bound(cuts, parts + 1, lo);
-    int i_hi = lower_bound(cuts, parts + 1, hi);
-    piece_off += 1 + (i_hi > i_lo ? fcum[i_hi] - fcum[i_lo] : 0);
+    piece_off += pieces_of(b);
   }
-  if (t == 0) split_indptr[bs] = totals[3];
+  if (t == 0) split_indptr[bs] = n_pieces;
 
   // 5. one table row per part
-  if (t < parts) {
+  for (int p = t; p < parts; p += kPlanThreads) {
     int row[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    int g0 = cuts[t], g1 = cuts[t + 1];
+    const int g0 = cuts[p], g1 = cuts[p + 1];
     if (g1 > g0) {
-      int b0 = upper_bound(pagecum, bs, g0) - 1;
-      int b1 = upper_bound(pagecum, bs, g1 - 1) - 1;
+      const int b0 = upper_bound(pagecum, bs, g0) - 1;
+      const int b1 = upper_bound(pagecum, bs, g1 - 1) - 1;
       row[0] = b0;
       row[1] = g0 - pagecum[b0];
       row[2] = b1;
       row[3] = g1 - pagecum[b1];
-      row[4] = fcum[upper_bound(cuts, parts + 1, g0)] - fcum[upper_bound(cuts, parts + 1, pagecum[b0])];
+      row[4] = fcum[upper_bound(cuts, parts + 1, g0)] -
+               fcum[upper_bound(cuts, parts + 1, pagecum[b0])];
       row[5] = g1 - g0;
     }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) tile_plan[t * 8 + k] = row[k];
+    int4* dst = reinterpret_cast<int4*>(tile_plan + p * 8);
+    dst[0] = make_int4(row[0], row[1], row[2], row[3]);
+    dst[1] = make_int4(row[4], row[5], row[6], row[7]);
   }
 }
 
@@ -196,9 +216,9 @@ extern "C" mla_status mla_plan_splits(const int32_t* seq_lens, int32_t bs, int32
   if (cus > 0 && num_parts > cus)
     return fail(MLA_ERR_CAPACITY, "mla_plan_splits: num_parts " + std::to_string(num_parts) +
                                       " exceeds the device's " + std::to_string(cus) + " CUs");
-  const int overhead = 1 + rows_per_req / 64;
+  const int overhead = plan_overhead_q(rows_per_req);
   const size_t lds = sizeof(int) * (2 * (size_t)(bs + 1) + (size_t)(num_parts + 1) +
-                                    (size_t)(num_parts + 2) + 16 + 4);
+                                    (size_t)(num_parts + 2) + kPlanWaves);
   static bool attr_set = false;
   if (!attr_set) {
     if (hipFuncSetAttribute((const void*)plan_splits_kernel,
