@@ -390,14 +390,15 @@ __device__ __forceinline__ void score_tile(f32x16& sc, uint32_t ka0,
 }
 
 // The output chain of a 32-key tile: 32 MFMAs (16 accumulator tiles x two
-// 16-key steps) in 8 groups of 4.  V^T operands come from three rotating
-// sets: group b uses set b % 3 and issues the reads of group b + 2 into set
-// (b + 2) % 3, then waits until at most those eight reads are outstanding,
-// i.e. until group b + 1's set has landed; each read has two groups (256
-// cycles) of matrix work to arrive.  An operand is two transposing 8-byte
+// 16-key steps) in 8 groups of 4.  V^T operands come from kPvRing rotating
+// sets: group b uses set b % kPvRing and issues the reads of group
+// b + kPvRing - 1 into the set group b - 1 used, then waits until group
+// b + 1's set has landed; each read has kPvRing - 1 groups (about 270 cycles)
+// of matrix work to arrive.  An operand is two transposing 8-byte
 // reads (keys kb..kb+3 and kb+4..kb+7 of the lane half) at va[0][par] + off
 // and va[1][par] + off.
 constexpr int kPvBlocks = 2 * kVTiles / 4;  // 8 groups of 4 MFMAs per 32-key tile
+constexpr int kPvRing = 3;                  // operand sets; reads run kPvRing - 1 groups ahead
 
 // LDS offsets (relative to va) of group nb's reads: MFMA i = 4 nb + j has
 // u = i / 16 (keys 8u..8u+7 of the lane half) and vt = i % 16; MFMAs j = 0, 1
@@ -452,28 +453,37 @@ __device__ __forceinline__ void pv_mfma(f32x16 (&oacc)[kVTiles], const VSet& s,
 }
 
 template <int T, int B, typename Hook, typename Pay, int... J>
-__device__ __forceinline__ void pv_group(f32x16 (&oacc)[kVTiles], VSet (&ring)[3],
+__device__ __forceinline__ void pv_group(f32x16 (&oacc)[kVTiles], VSet (&ring)[kPvRing],
                                          const bf16x8 (&pop)[2], const uint32_t (&va)[2][2],
                                          Hook& hook, Pay& pay, std::integer_sequence<int, J...>) {
-  if constexpr (B + 2 < kPvBlocks) v_reads<T, B + 2>(ring[(B + 2) % 3], va);
+  constexpr int kAhead = kPvRing - 1;
+  if constexpr (B + kAhead < kPvBlocks)
+    v_reads<T, B + kAhead>(ring[(B + kAhead) % kPvRing], va);
   MLA_SB();
-  (pv_mfma<B, J>(oacc, ring[B % 3], pop, pay), ...);
-  if constexpr (B + 2 < kPvBlocks)
-    v_wait<8>(ring[(B + 1) % 3]);
-  else if constexpr (B + 1 < kPvBlocks)
-    v_wait<0>(ring[(B + 1) % 3]);
-  else
+  (pv_mfma<B, J>(oacc, ring[B % kPvRing], pop, pay), ...);
+  if constexpr (B + 1 < kPvBlocks) {
+    // reads issued after group B+1's: groups B+2 .. min(B+kAhead, last)
+    constexpr int last = (B + kAhead < kPvBlocks) ? B + kAhead : kPvBlocks - 1;
+    v_wait<8 * (last - (B + 1))>(ring[(B + 1) % kPvRing]);
+  } else {
     mfma_tail();
+  }
   MLA_SB();
   hook(ic<B>{});
   MLA_SB();
 }
 
 template <int T, typename Hook, typename Pay, int... B>
-__device__ __forceinline__ void pv_chain(f32x16 (&oacc)[kVTiles], VSet (&ring)[3],
+__device__ __forceinline__ void pv_chain(f32x16 (&oacc)[kVTiles], VSet (&ring)[kPvRing],
                                          const bf16x8 (&pop)[2], const uint32_t (&va)[2][2],
                                          Hook& hook, Pay& pay, std::integer_sequence<int, B...>) {
   (pv_group<T, B>(oacc, ring, pop, va, hook, pay, std::make_integer_sequence<int, 4>{}), ...);
+}
+
+template <int T, int... B>
+__device__ __forceinline__ void pv_prologue(VSet (&ring)[kPvRing], const uint32_t (&va)[2][2],
+                                            std::integer_sequence<int, B...>) {
+  (v_reads<T, B>(ring[B], va), ...);
 }
 
 // O^T += V^T P^T for 32-key tile T: 32 MFMAs.  pay(ic<s>) runs after MFMA s
@@ -485,10 +495,9 @@ __device__ __forceinline__ void pv_tile(f32x16 (&oacc)[kVTiles], const bf16x8 (&
                                         uint32_t va0, Hook&& hook, Pay&& pay) {
   const uint32_t va10 = (va0 + 512u) ^ 32u;
   const uint32_t va[2][2] = {{va0, va0 ^ 64u}, {va10, va10 ^ 64u}};
-  VSet ring[3];
-  v_reads<T, 0>(ring[0], va);
-  v_reads<T, 1>(ring[1], va);
-  v_wait<8>(ring[0]);
+  VSet ring[kPvRing];
+  pv_prologue<T>(ring, va, std::make_integer_sequence<int, kPvRing - 1>{});
+  v_wait<8 * (kPvRing - 2)>(ring[0]);
   MLA_SB();
   pv_chain<T>(oacc, ring, pop, va, hook, pay, std::make_integer_sequence<int, kPvBlocks>{});
 }
@@ -644,34 +653,34 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
   __syncthreads();
 
   // ---- page cursor for prefetch ----------------------------------------------
-  // (nb, np) is the page whose loads are issued next; its block-table entry
-  // and length were read one page earlier so the scalar loads never stall.
+  // (nb, np) is the page whose loads are issued next.  Its block-table entry
+  // (nraw) is read a whole page before it is used, and only checked when
+  // used, so the scalar load never holds up the wave.
   int nb = b_first, np = pg_first;
   int nlen = seq_lens[nb];
   int nend = (nb == b_last) ? pg_last : page_count(nlen);
-  auto phys_of = [&](int b, int p) -> int64_t {
-    if (p >= P.bt_stride) return 0;
-    const int64_t pg = block_table[(int64_t)b * P.bt_stride + p];
-    return (pg >= 0 && pg < P.num_pages) ? pg : 0;
+  auto raw_of = [&](int b, int p) -> int32_t {
+    return p < P.bt_stride ? block_table[(int64_t)b * P.bt_stride + p] : 0;
   };
-  int64_t nphys = phys_of(nb, np);
+  int32_t nraw = raw_of(nb, np);
+  // the cursor's physical page; entries outside the pool read page 0
+  auto nphys = [&]() -> int64_t { return (nraw >= 0 && nraw < P.num_pages) ? nraw : 0; };
   int nrows = min(kPage, max(0, nlen - np * kPage));
   // Loads of the cursor's page into LDS for page index `j` of the part.
   auto issue = [&](int j) {
     const int vr = __builtin_amdgcn_readfirstlane(nrows);
     if constexpr (FP8)
       issue_loads_f8(std::make_integer_sequence<int, kLoadsPerWaveF8>{},
-                     page_rsrc<kD>(kv + nphys * kSrcPageBytes, vr),
+                     page_rsrc<kD>(kv + nphys() * kSrcPageBytes, vr),
                      smem + kPageBytes + (j & 1) * kPageBytesF8, wave, wave * 1024 + 16 * lane);
     else {
       const uint32_t lo = lane_offsets(lane, wave).load;
-      issue_page_loads(page_rsrc<kRowBytes>(kv + nphys * kSrcPageBytes, vr),
+      issue_page_loads(page_rsrc<kRowBytes>(kv + nphys() * kSrcPageBytes, vr),
                        smem + (j & 1) * kPageBytes, wave, lo, lo + 4 * (8 * kRowBytes));
     }
   };
-  // Move the cursor one page on and read that page's block-table entry and
-  // length.  Called after a page's compute, so the scalar loads have a whole
-  // barrier interval to land before the next issue needs them.
+  // Move the cursor one page on and start reading that page's block-table
+  // entry (a new request's length is needed at once, once per request).
   auto advance = [&]() {
     ++np;
     while (np >= nend && nb < b_last) {
@@ -680,7 +689,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
       nlen = seq_lens[nb];
       nend = (nb == b_last) ? pg_last : page_count(nlen);
     }
-    nphys = phys_of(nb, np);
+    nraw = raw_of(nb, np);
     nrows = min(kPage, max(0, nlen - np * kPage));
   };
 
@@ -761,10 +770,13 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
       // drains them.
       const bool has_next = it + 1 < total;
       const __amdgpu_buffer_rsrc_t next_rsrc =
-          page_rsrc<FP8 ? kD : kRowBytes>(kv + nphys * kSrcPageBytes,
+          page_rsrc<FP8 ? kD : kRowBytes>(kv + nphys() * kSrcPageBytes,
                                            __builtin_amdgcn_readfirstlane(nrows));
       uint8_t* const next_buf = FP8 ? smem + kPageBytes + ((it + 1) & 1) * kPageBytesF8
                                     : smem + ((it + 1) & 1) * kPageBytes;
+      // The cursor moves on to page it + 2 now: its block-table entry then has
+      // this whole page to arrive.
+      if (it + 1 < total) advance();
       const uint32_t plane = pinned_lane();
       const LaneOffsets lo = lane_offsets(plane, wave);
       // load K of this wave's share, K < 18 (bf16) or K < 9 (e4m3)
@@ -845,7 +857,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
           need = m_tile > m_run + kTau;
           if (__any(need)) {
             const float m_new = need ? m_tile : m_run;
-            const float alpha = need ? exp2f(m_run - m_new) : 1.0f;
+            const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
             l_run *= alpha;
             if (__any(need && m_run != -INFINITY)) {
 #pragma unroll
@@ -944,7 +956,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
           const bool need = m_tile > m_run + kTau;
           if (__any(need)) {
             const float m_new = need ? m_tile : m_run;
-            const float alpha = need ? exp2f(m_run - m_new) : 1.0f;
+            const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
             l_run *= alpha;
             // Rows whose running max is still -inf have o = 0: only a wave with
             // some earlier weight needs the 256-register rescale.
@@ -981,7 +993,6 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
             pv_tile<1>(oacc, pop, va, no_hook, NoSlot{});
         }
       }
-      if (it + 1 < total) advance();
     };
     const int cfast = min(cend, max(cp, first_masked));
     for (; cp < cfast && it < total; ++cp, ++it) page(std::false_type{});
