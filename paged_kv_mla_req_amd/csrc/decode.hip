@@ -502,6 +502,14 @@ __device__ __forceinline__ void pv_tile(f32x16 (&oacc)[kVTiles], const bf16x8 (&
   pv_chain<T>(oacc, ring, pop, va, hook, pay, std::make_integer_sequence<int, kPvBlocks>{});
 }
 
+// Element placed in payload slot 8 + d when 16 elements are spread over 27
+// slots (element i at 8 + 7i/4), or -1.
+__host__ __device__ constexpr int spread_slot_elem(int d) {
+  for (int i = 0; i < 16; ++i)
+    if ((7 * i) / 4 == d) return i;
+  return -1;
+}
+
 // Max / sum over the two lane halves (which hold the same query row's other
 // keys), exchanged with v_permlane32_swap.
 __device__ __forceinline__ float xhalf_max(float x) {
@@ -870,13 +878,16 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
           for (int j = 0; j < 4; ++j) ls[j] = 0.f;
         };
         float pf[2];
+        // weights of tile 0 spread over slots 8..34 (element i at 8 + 7i/4), so
+        // that each MFMA shadow holds at most one exp
         auto pay_s1 = [&](auto slot) {
           constexpr int k = decltype(slot)::value;
+          constexpr int i = spread_slot_elem(k - 8);
           if constexpr (k <= 4)
             max_slots(sc0, slot);
-          else if constexpr (k >= 8 && k < 24)
-            weight(sc0, ic<k - 8>{}, pf);
-          else if constexpr (k == 24) {
+          else if constexpr (k >= 8 && i >= 0)
+            weight(sc0, ic<i>{}, pf);
+          else if constexpr (k == 35) {
             l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
             pin(l_run);
           }
@@ -906,13 +917,15 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
                                             __builtin_convertvector((f32x2){pf[0], pf[1]}, bf16x2));
         }
         pop[0] = __builtin_bit_cast(bf16x8, (u32x4){pk[0], pk[1], pk[2], pk[3]});
+        // weights of keys 16..31 at every other slot of groups 0..3 (used from
+        // group 4 on)
         auto pay_pv1 = [&](auto slot) {
           constexpr int k = decltype(slot)::value;
-          if constexpr (k < 8) {
-            weight(sc1, ic<k + 8>{}, pf);
-            if constexpr (k == 7)
+          if constexpr (k < 16 && k % 2 == 0) {
+            weight(sc1, ic<k / 2 + 8>{}, pf);
+            if constexpr (k == 14)
               pop[1] = __builtin_bit_cast(bf16x8, (u32x4){pk[4], pk[5], pk[6], pk[7]});
-          } else if constexpr (k == 8) {
+          } else if constexpr (k == 15) {
             l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
             pin(l_run);
           }
