@@ -203,6 +203,15 @@ __device__ __forceinline__ void convert_f8_page(const uint8_t* stage, uint8_t* b
   }
 }
 
+// Read an index-array entry that is the same for every lane of the wave
+// through the scalar cache.  The index arrays are never written while the
+// kernel runs; the compiler cannot prove that for reads after the first
+// output stores and would otherwise use a vector load and a full wait.
+__device__ __forceinline__ int32_t uniform_load(const int32_t* p, int i) {
+  using const_i32 = const __attribute__((address_space(4))) int32_t;
+  return *((const_i32*)p + __builtin_amdgcn_readfirstlane(i));
+}
+
 __device__ __forceinline__ int32_t page_count(int32_t L) {
   return L > 0 ? (L + kPage - 1) / kPage : 0;
 }
@@ -665,7 +674,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
   // (nraw) is read a whole page before it is used, and only checked when
   // used, so the scalar load never holds up the wave.
   int nb = b_first, np = pg_first;
-  int nlen = seq_lens[nb];
+  int nlen = uniform_load(seq_lens, nb);
   int nend = (nb == b_last) ? pg_last : page_count(nlen);
   auto raw_of = [&](int b, int p) -> int32_t {
     return p < P.bt_stride ? block_table[(int64_t)b * P.bt_stride + p] : 0;
@@ -694,7 +703,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
     while (np >= nend && nb < b_last) {
       ++nb;
       np = 0;
-      nlen = seq_lens[nb];
+      nlen = uniform_load(seq_lens, nb);
       nend = (nb == b_last) ? pg_last : page_count(nlen);
     }
     nraw = raw_of(nb, np);
@@ -738,23 +747,27 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
   int piece = first_piece;
   while (true) {
     // ---- one piece: pages [cp, cend) of request cb ---------------------------
-    const int32_t L = seq_lens[cb];
+    const int32_t L = uniform_load(seq_lens, cb);
     const int cend = (cb == b_last) ? pg_last : page_count(L);
     // pages from first_masked on may hold keys some row of this wave cannot see
     const int32_t lim_min = P.causal ? L - P.q_len + i_tok_min : L - 1;
     const int first_masked =
         __builtin_amdgcn_readfirstlane(lim_min >= 0 ? (lim_min + 1) / kPage : 0);
     {
+      // A lane whose row is past the last one reads row 0 instead: its results
+      // stay in that lane's row of the accumulators and are never stored, so
+      // (bf16) no select on the loaded values makes the wave wait for them here.
       const uint32_t ql = pinned_lane();
       const int r = row0 + (int)(ql & 31);
-      const bool row_valid = r < P.rows;
       const uint16_t* qrow =
-          q + ((int64_t)cb * P.rows + (row_valid ? r : 0)) * kD + 8 * (int)(ql >> 5);
+          q + ((int64_t)cb * P.rows + (r < P.rows ? r : 0)) * kD + 8 * (int)(ql >> 5);
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
         u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 16 * ks);
         if (FP8) v ^= q_sign;
-        if (!row_valid) v = (u32x4){0, 0, 0, 0};
+        // (the e4m3 kernel keeps the select: without it the compiler spills an
+        // accumulator tile around the epilogue)
+        if (FP8 && !(r < P.rows)) v = (u32x4){0, 0, 0, 0};
         qreg[ks] = __builtin_bit_cast(bf16x8, v);
       }
     }
@@ -1017,8 +1030,8 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
       const float inv = l_tot > 0.f ? delta / l_tot : 0.f;
       const float lse_val =
           l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
-      const int k0 = split_indptr[cb];
-      const int k = split_indptr[cb + 1] - k0;
+      const int k0 = uniform_load(split_indptr, cb);
+      const int k = uniform_load(split_indptr, cb + 1) - k0;
       const int64_t slot = (int64_t)k0 + piece;
       // A piece of a split request goes to its partial slot (normalised o and
       // lse, fp32); the only piece of a request is final (bf16 o).
@@ -1037,7 +1050,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
     // next request of the part that has pages
     do {
       ++cb;
-    } while (cb < b_last && page_count(seq_lens[cb]) <= 0);
+    } while (cb < b_last && page_count(uniform_load(seq_lens, cb)) <= 0);
     cp = 0;
     piece = 0;
   }
