@@ -276,13 +276,17 @@ __device__ __forceinline__ void scale_tile(f32x16& acc, float alpha) {
 template <int N>
 using ic = std::integral_constant<int, N>;
 
-// Pins values to a point of the instruction stream: an empty volatile
-// statement that claims to modify them.  Payload code reads its inputs
-// through one and hands its results to one, so the compiler can move it
-// neither above nor below its slot (scheduling barriers alone do not stop
-// sinking of pure arithmetic into later blocks).
-__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+// pin(x): an empty volatile statement that claims to modify x, so that
+// nothing computed from x can move above it (used for the lane id, so that
+// per-lane offsets are recomputed where they are needed).
+// keep(x): an empty volatile statement that reads x, so that x is computed
+// before it.  Payload code hands its results to one: with the scheduling
+// barriers around each slot that confines the payload to its slot
+// (scheduling barriers alone do not stop sinking of pure arithmetic into
+// later blocks).  Unlike pin(), it costs no copy and no wait state.
 __device__ __forceinline__ void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void keep(float x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void keep(uint32_t x) { asm volatile("" ::"v"(x)); }
 
 struct NoSlot {
   template <int N>
@@ -294,18 +298,24 @@ struct NoSlot {
 template <bool FIRST>
 __device__ __forceinline__ void mfma_s(f32x16& c, const bf16x8& a, const bf16x8& b) {
   if constexpr (FIRST)
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
                  : "=&v"(c)
                  : "v"(a), "v"(b));
   else
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
                  : "+v"(c)
                  : "v"(a), "v"(b));
 }
 
-// O^T MFMA, accumulator tile in AGPRs.
+// O^T MFMA, accumulator tile in AGPRs.  FRESH: the weights p were just
+// written by VALU instructions (packing), which need 2 wait states before an
+// MFMA reads them.
+template <bool FRESH = false>
 __device__ __forceinline__ void mfma_o(f32x16& o, const bf16x8& v, const bf16x8& p) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(v), "v"(p));
+  if constexpr (FRESH)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(v), "v"(p));
+  else
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(v), "v"(p));
 }
 
 __device__ __forceinline__ void mfma_tail() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
@@ -313,10 +323,11 @@ __device__ __forceinline__ void mfma_tail() { asm volatile("s_nop 7\n\ts_nop 7\n
 // S^T chain: one 16-byte K-operand read per MFMA, from a ring of kKRing
 // operand slots.  The read for k-step ks+kKAhead is issued right after
 // MFMA ks, into the slot MFMA ks-1 used (its operands were read when it
-// issued, a full MFMA earlier), and MFMA ks+1 first waits until its own
-// read has landed -- so every read has about kKAhead MFMAs (~230 cycles) to
-// arrive, with one wait per MFMA.
-constexpr int kKRing = 8;
+// issued, a full MFMA earlier); after every second MFMA one wait covers the
+// reads of the next two -- so every read has at least kKAhead - 2 MFMAs to
+// arrive.  (A single wave per SIMD issues at most one instruction per
+// 4-cycle turn: the chain is kept to the instructions it needs.)
+constexpr int kKRing = 9;
 constexpr int kKAhead = kKRing - 1;
 
 // K operand of k-step KS of the tile at byte offset TB: 16 bytes at
@@ -335,16 +346,21 @@ __device__ __forceinline__ void k_read(bf16x8& dst, const uint32_t (&a)[4]) {
   }
 }
 
-// Wait until at most N LDS reads are outstanding; x is usable after it.
+// Wait until at most N LDS reads are outstanding (x is usable after it).  A
+// plain wait instruction: the reads and their consumers are volatile
+// statements, which keep their order around it, and an inline-assembly wait
+// claiming to write x would cost a wait state before the MFMA reading x.
 template <int N>
-__device__ __forceinline__ void lds_wait(bf16x8& x) {
-  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "i"(N));
+__device__ __forceinline__ void lgkm_wait() {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+  __builtin_amdgcn_s_waitcnt(0xC07F | (N << 8));
 }
 
 // Step KS of the S^T chain of the tile at TB: MFMA KS, payload slot KS, the
-// read for KS + kKAhead, the wait for KS + 1, and hook(KS / 4) after every
-// fourth MFMA (the waits leave no read in flight across a hook only at the
-// end of the chain, so hooks must not touch LDS reads).
+// read for KS + kKAhead, after an odd KS the wait for KS + 1 and KS + 2, and
+// hook(KS / 4) after every fourth MFMA (the waits leave no read in flight
+// across a hook only at the end of the chain, so hooks must not touch LDS
+// reads).
 template <int TB, int KS, typename Hook, typename Pay>
 __device__ __forceinline__ void s_step(f32x16& sc, bf16x8 (&ring)[kKRing],
                                        const bf16x8 (&qreg)[kKSteps], const uint32_t (&a)[4],
@@ -355,12 +371,13 @@ __device__ __forceinline__ void s_step(f32x16& sc, bf16x8 (&ring)[kKRing],
   MLA_SB();
   if constexpr (KS + kKAhead < kKSteps) k_read<TB, KS + kKAhead>(ring[(KS + kKAhead) % kKRing], a);
   MLA_SB();
-  if constexpr (KS + 1 < kKSteps) {
-    // reads issued after the one for KS + 1: KS + 2 .. min(KS + kKAhead, last)
-    constexpr int last = (KS + kKAhead < kKSteps) ? KS + kKAhead : kKSteps - 1;
-    lds_wait<last - (KS + 1)>(ring[(KS + 1) % kKRing]);
-  } else {
+  if constexpr (KS + 1 == kKSteps) {
     mfma_tail();
+  } else if constexpr (KS % 2 == 1) {
+    // reads issued after the ones for KS + 1 and KS + 2
+    constexpr int last = (KS + kKAhead < kKSteps) ? KS + kKAhead : kKSteps - 1;
+    constexpr int need = (KS + 2 < kKSteps) ? KS + 2 : KS + 1;
+    lgkm_wait<last - need>();
   }
   MLA_SB();
   if constexpr (KS % 4 == 3) {
@@ -393,7 +410,7 @@ __device__ __forceinline__ void score_tile(f32x16& sc, uint32_t ka0,
   const uint32_t a[4] = {ka0, ka0 ^ 32u, ka0 ^ 64u, ka0 ^ 96u};
   bf16x8 ring[kKRing];
   s_prologue<TB>(ring, a, std::make_integer_sequence<int, kKAhead>{});
-  lds_wait<kKAhead - 1>(ring[0]);
+  lgkm_wait<kKAhead - 2>();  // k-steps 0 and 1
   MLA_SB();
   s_steps<TB>(sc, ring, qreg, a, hook, pay, std::make_integer_sequence<int, kKSteps>{});
 }
@@ -443,11 +460,8 @@ __device__ __forceinline__ void v_reads(VSet& s, const uint32_t (&va)[2][2]) {
 
 // Wait until at most N LDS reads are outstanding; s becomes usable after it.
 template <int N>
-__device__ __forceinline__ void v_wait(VSet& s) {
-  asm volatile("s_waitcnt lgkmcnt(%8)"
-               : "+v"(s.lo[0]), "+v"(s.lo[1]), "+v"(s.lo[2]), "+v"(s.lo[3]), "+v"(s.hi[0]),
-                 "+v"(s.hi[1]), "+v"(s.hi[2]), "+v"(s.hi[3])
-               : "i"(N));
+__device__ __forceinline__ void v_wait(VSet&) {
+  lgkm_wait<N>();
 }
 
 // MFMA J of group B of an output chain, then payload slot 4B+J.
@@ -455,7 +469,8 @@ template <int B, int J, typename Pay>
 __device__ __forceinline__ void pv_mfma(f32x16 (&oacc)[kVTiles], const VSet& s,
                                         const bf16x8 (&pop)[2], Pay& pay) {
   constexpr int u = (4 * B) / kVTiles, vt = (4 * B) % kVTiles + J;
-  mfma_o(oacc[vt], __builtin_shufflevector(s.lo[J], s.hi[J], 0, 1, 2, 3, 4, 5, 6, 7), pop[u]);
+  mfma_o<(4 * B + J) % kVTiles == 0>(
+      oacc[vt], __builtin_shufflevector(s.lo[J], s.hi[J], 0, 1, 2, 3, 4, 5, 6, 7), pop[u]);
   MLA_SB();
   pay(ic<4 * B + J>{});
   MLA_SB();
@@ -509,6 +524,154 @@ __device__ __forceinline__ void pv_tile(f32x16 (&oacc)[kVTiles], const bf16x8 (&
   v_wait<8 * (kPvRing - 2)>(ring[0]);
   MLA_SB();
   pv_chain<T>(oacc, ring, pop, va, hook, pay, std::make_integer_sequence<int, kPvBlocks>{});
+}
+
+// ---- the second score tile and the first output tile as one chain ----------
+// On its own an output tile is bound by its transposing V^T reads (two per
+// MFMA) and a score tile by the matrix pipe (one K read per MFMA).  Mixing
+// the two, slot by slot, keeps the matrix pipe busy through both.  Slot s
+// holds one MFMA: the first kCPrefix slots are score MFMAs of tile 1 (while
+// the weights of tile 0 are computed in their shadow), the next kCMixed
+// slots spread the remaining score MFMAs evenly among output MFMAs of tile
+// 0, and the rest are output MFMAs (in whose shadow the row max and the
+// first weights of tile 1 are computed).  Every slot reads 16 bytes of
+// operand per lane (one K read, or two 8-byte V^T reads), kCAhead slots
+// before its MFMA; the reads are waited for two slots at a time.
+constexpr int kCSlots = kKSteps + 2 * kVTiles;  // 36 score + 32 output MFMAs
+constexpr int kCPrefix = 9;
+constexpr int kCMixed = 50;
+constexpr int kCAhead = 8;
+
+__host__ __device__ constexpr bool cs_is_s(int s) {
+  if (s < kCPrefix) return true;
+  if (s >= kCPrefix + kCMixed) return false;
+  const int t = s - kCPrefix, n = kKSteps - kCPrefix;
+  return (t + 1) * n / kCMixed != t * n / kCMixed;
+}
+// index of slot s's MFMA within its own chain (k-step, or output MFMA)
+__host__ __device__ constexpr int cs_index(int s) {
+  int c = 0;
+  for (int u = 0; u < s; ++u) c += (cs_is_s(u) == cs_is_s(s)) ? 1 : 0;
+  return c;
+}
+__host__ __device__ constexpr int cs_reads(int s) { return cs_is_s(s) ? 1 : 2; }
+// The wait before slot s (s even) covers slots s and s + 1: LDS reads issued
+// after slot s + 1's, i.e. those of slots s+2 .. s+kCAhead-1 (the reads of
+// slots up to s - 1 + kCAhead are out by then).
+__host__ __device__ constexpr int cs_wait(int s) {
+  int n = 0;
+  for (int u = s + 2; u < s + kCAhead && u < kCSlots; ++u) n += cs_reads(u);
+  return n;
+}
+__host__ __device__ constexpr int cs_slot_of(bool score, int index) {
+  for (int s = 0; s < kCSlots; ++s)
+    if (cs_is_s(s) == score && cs_index(s) == index) return s;
+  return -1;
+}
+__host__ __device__ constexpr bool cs_layout_ok() {
+  int ns = 0, wmax = 0;
+  for (int s = 0; s < kCSlots; ++s) {
+    ns += cs_is_s(s) ? 1 : 0;
+    if (s % 2 == 0) wmax = cs_wait(s) > wmax ? cs_wait(s) : wmax;
+  }
+  return ns == kKSteps && wmax <= 15;
+}
+static_assert(cs_layout_ok() && kCSlots % 2 == 0,
+              "combined chain: 36 score slots, waits within lgkmcnt range");
+constexpr int kCLastScore = cs_slot_of(true, kKSteps - 1);  // 54
+constexpr int kCFirstOut = cs_slot_of(false, 0);            // 13
+constexpr int kCOutU1 = cs_slot_of(false, kVTiles);         // 48: first MFMA on keys 16..31
+
+struct COps {
+  bf16x8 k[kCSlots];            // score slots
+  bf16x4 lo[kCSlots], hi[kCSlots];  // output slots
+};
+
+// Operand reads of slot S: the K read of tile 1 (byte offset 32 * 128), or
+// the two V^T reads of output MFMA j of tile 0 (accumulator tile j % 16,
+// keys 8 (j / 16) .. +7 of the lane half; see pv_tile for the addresses).
+template <int S>
+__device__ __forceinline__ void c_read(COps& op, const uint32_t (&a)[4],
+                                       const uint32_t (&va)[2][2]) {
+  if constexpr (cs_is_s(S)) {
+    k_read<32 * 128, cs_index(S)>(op.k[S], a);
+  } else {
+    constexpr int j = cs_index(S), vt = j % kVTiles, u = j / kVTiles;
+    constexpr int off = 8 * u * 128 + 8192 * (vt >> 1);
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %2 offset:%4\n\t"
+        "ds_read_b64_tr_b16 %1, %3 offset:%4"
+        : "=&v"(op.lo[S]), "=&v"(op.hi[S])
+        : "v"(va[0][vt & 1]), "v"(va[1][vt & 1]), "i"(off));
+  }
+}
+
+template <int S>
+__device__ __forceinline__ void c_wait() {
+  lgkm_wait<cs_wait(S)>();
+}
+
+// Slot S: its MFMA, pay(ic<S>) in its shadow, the reads of slot S + kCAhead,
+// after an odd slot the wait for the next two, then hook(ic<S>).
+template <int S, typename Hook, typename Pay>
+__device__ __forceinline__ void c_step(f32x16& sc, f32x16 (&oacc)[kVTiles], COps& op,
+                                       const bf16x8 (&pop)[2], const bf16x8 (&qreg)[kKSteps],
+                                       const uint32_t (&a)[4], const uint32_t (&va)[2][2],
+                                       Hook& hook, Pay& pay) {
+  if constexpr (cs_is_s(S)) {
+    constexpr int ks = cs_index(S);
+    mfma_s<ks == 0>(sc, op.k[S], qreg[ks]);
+  } else {
+    constexpr int j = cs_index(S);
+    mfma_o<j % kVTiles == 0>(oacc[j % kVTiles],
+                             __builtin_shufflevector(op.lo[S], op.hi[S], 0, 1, 2, 3, 4, 5, 6, 7),
+                             pop[j / kVTiles]);
+  }
+  MLA_SB();
+  pay(ic<S>{});
+  MLA_SB();
+  if constexpr (S + kCAhead < kCSlots) c_read<S + kCAhead>(op, a, va);
+  MLA_SB();
+  if constexpr (S + 1 == kCSlots)
+    mfma_tail();
+  else if constexpr (S % 2 == 1)
+    c_wait<S + 1>();
+  MLA_SB();
+  hook(ic<S>{});
+  MLA_SB();
+}
+
+template <typename Hook, typename Pay, int... S>
+__device__ __forceinline__ void c_steps(f32x16& sc, f32x16 (&oacc)[kVTiles], COps& op,
+                                        const bf16x8 (&pop)[2], const bf16x8 (&qreg)[kKSteps],
+                                        const uint32_t (&a)[4], const uint32_t (&va)[2][2],
+                                        Hook& hook, Pay& pay, std::integer_sequence<int, S...>) {
+  (c_step<S>(sc, oacc, op, pop, qreg, a, va, hook, pay), ...);
+}
+
+template <int... S>
+__device__ __forceinline__ void c_prologue(COps& op, const uint32_t (&a)[4],
+                                           const uint32_t (&va)[2][2],
+                                           std::integer_sequence<int, S...>) {
+  (c_read<S>(op, a, va), ...);
+}
+
+// S^T of tile 1 into sc and O^T += V^T P^T for tile 0 (pop: its weights,
+// pop[0] used from slot kCFirstOut, pop[1] from slot kCOutU1), ka0 / va0 as
+// for score_tile / pv_tile.
+template <typename Hook, typename Pay>
+__device__ __forceinline__ void combined_chain(f32x16& sc, f32x16 (&oacc)[kVTiles],
+                                               const bf16x8 (&pop)[2],
+                                               const bf16x8 (&qreg)[kKSteps], uint32_t ka0,
+                                               uint32_t va0, Hook&& hook, Pay&& pay) {
+  const uint32_t a[4] = {ka0, ka0 ^ 32u, ka0 ^ 64u, ka0 ^ 96u};
+  const uint32_t va10 = (va0 + 512u) ^ 32u;
+  const uint32_t va[2][2] = {{va0, va0 ^ 64u}, {va10, va10 ^ 64u}};
+  COps op;
+  c_prologue(op, a, va, std::make_integer_sequence<int, kCAhead>{});
+  c_wait<0>();
+  MLA_SB();
+  c_steps(sc, oacc, op, pop, qreg, a, va, hook, pay, std::make_integer_sequence<int, kCSlots>{});
 }
 
 // Element placed in payload slot 8 + d when 16 elements are spread over 27
@@ -831,9 +994,10 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
         // ---- no key of this page is masked for any row of the wave ----------------
         // The softmax of each tile runs in the shadow of the matrix work:
         //   S(0)
-        //   S(1)  | max(0), rescale decision (between groups), weights P(0)
-        //   PV(0) | max(1)
-        //   rescale decision, weights P(1) for keys 0..15 of the tile
+        //   S(1) + PV(0) mixed | max(0), rescale decision, weights P(0);
+        //                        then max(1) and P(1) for keys 0..15 of the tile,
+        //                        under the running max as it stands
+        //   (rare: the running max moves for tile 1 -> rescale, redo those weights)
         //   PV(1) | weights P(1) for keys 16..31 (used from group 4 on)
         // sc0[i] / sc1[i] is key 16h + i of tile 0 / 1.
         f32x16 sc0, sc1;
@@ -843,104 +1007,122 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
         float m_tile = 0.f, neg_m = 0.f;
         bool need = false;
         uint32_t pk[8];
-        // row max of tile `sc` in slots 0..4: m_tile, need
-        auto max_slots = [&](const f32x16& sc, auto slot) {
-          constexpr int k = decltype(slot)::value;
+        // row max of tile `sc`, part k (k < 4: 4 of the 16 values; k == 4: the
+        // rest): m_tile
+        auto max_part = [&](const f32x16& sc, auto part) {
+          constexpr int k = decltype(part)::value;
           if constexpr (k < 4) {
-            float x0 = sc[k], x1 = sc[k + 4], x2 = sc[k + 8], x3 = sc[k + 12];
-            pin(x0), pin(x1), pin(x2), pin(x3);
-            mx[k] = fmaxf(fmaxf(x0, x1), fmaxf(x2, x3));
-            pin(mx[k]);
-          } else if constexpr (k == 4) {
+            mx[k] = fmaxf(fmaxf(sc[k], sc[k + 4]), fmaxf(sc[k + 8], sc[k + 12]));
+            keep(mx[k]);
+          } else {
             const float mloc = xhalf_max(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])));
             m_tile = c_log2 * mloc;
-            pin(m_tile);
+            keep(m_tile);
           }
         };
-        // weight of element i of tile `sc`; pairs are packed to bf16
-        auto weight = [&](const f32x16& sc, auto ii, float (&pf)[2]) {
+        // weights of elements i, i + 1 of tile `sc` (i even), packed to bf16 in
+        // pk[i / 2]; their sum goes to ls
+        auto weight2 = [&](const f32x16& sc, auto ii) {
           constexpr int i = decltype(ii)::value;
-          float x = sc[i];
-          pin(x);
-          const float pv = __builtin_amdgcn_exp2f(fmaf(x, c_log2, neg_m));
-          ls[i & 3] += pv;
-          pin(ls[i & 3]);
-          pf[i & 1] = pv;
-          if constexpr (i & 1) {
-            pk[i >> 1] = __builtin_bit_cast(uint32_t,
-                                            __builtin_convertvector((f32x2){pf[0], pf[1]}, bf16x2));
-            pin(pk[i >> 1]);
-          }
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[i], c_log2, neg_m));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[i + 1], c_log2, neg_m));
+          ls[i & 3] += p0;
+          ls[(i + 1) & 3] += p1;
+          keep(ls[i & 3]), keep(ls[(i + 1) & 3]);
+          pk[i >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p0, p1}, bf16x2));
+          keep(pk[i >> 1]);
         };
-        // lazy rescale: move the running max only when the tile's max exceeds it by
-        // more than kTau (p <= 2^kTau otherwise); rows still at -inf have o = 0
-        auto decide = [&]() {
-          need = m_tile > m_run + kTau;
-          if (__any(need)) {
-            const float m_new = need ? m_tile : m_run;
-            const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-            l_run *= alpha;
-            if (__any(need && m_run != -INFINITY)) {
-#pragma unroll
-              for (int vt = 0; vt < kVTiles; ++vt) scale_tile(oacc[vt], alpha);
-            }
-            m_run = m_new;
-          }
-          neg_m = -m_run;  // finite: this tile has a finite max
+        auto fold_ls = [&]() {
+          l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+          keep(l_run);
 #pragma unroll
           for (int j = 0; j < 4; ++j) ls[j] = 0.f;
         };
-        float pf[2];
-        // weights of tile 0 spread over slots 8..34 (element i at 8 + 7i/4), so
-        // that each MFMA shadow holds at most one exp
-        auto pay_s1 = [&](auto slot) {
+        // lazy rescale: move the running max only when the tile's max exceeds it by
+        // more than kTau (p <= 2^kTau otherwise); rows still at -inf have o = 0.
+        // Call only with no output MFMA in flight.
+        auto rescale = [&]() {
+          const float m_new = need ? m_tile : m_run;
+          const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+          l_run *= alpha;
+          if (__any(need && m_run != -INFINITY)) {
+#pragma unroll
+            for (int vt = 0; vt < kVTiles; ++vt) scale_tile(oacc[vt], alpha);
+          }
+          m_run = m_new;
+          neg_m = -m_run;  // finite: this tile has a finite max
+        };
+        bf16x8 pop[2];
+        // payload slots of the combined chain
+        constexpr int kE0 = 5;                 // tile 0, keys 0..7: slots 5..8
+        constexpr int kE1 = kCPrefix + 1;      // tile 0, keys 8..15: slots 10, 16, 22, 28
+        constexpr int kLd = kCPrefix + 2;      // next-page loads 9..17: slots 11, 14, .., 35
+        constexpr int kM1 = kCLastScore + 1;   // max(1): slots 59..63
+        constexpr int kW1 = kM1 + 5;           // tile 1, keys 0..7: slots 64..67
+        static_assert(kE0 + 4 == kCPrefix && kCPrefix == kCFirstOut && kE1 + 6 * 3 < kCOutU1 &&
+                          kW1 + 4 == kCSlots,
+                      "combined chain payload layout");
+        auto pay_c = [&](auto slot) {
           constexpr int k = decltype(slot)::value;
-          constexpr int i = spread_slot_elem(k - 8);
-          if constexpr (k <= 4)
-            max_slots(sc0, slot);
-          else if constexpr (k >= 8 && i >= 0)
-            weight(sc0, ic<i>{}, pf);
-          else if constexpr (k == 35) {
-            l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-            pin(l_run);
+          if constexpr (k < kE0) {
+            max_part(sc0, slot);
+          } else if constexpr (k < kE0 + 4) {
+            weight2(sc0, ic<2 * (k - kE0)>{});
+            if constexpr (k == kE0 + 3)
+              pop[0] = __builtin_bit_cast(bf16x8, (u32x4){pk[0], pk[1], pk[2], pk[3]});
+          } else if constexpr (k >= kE1 && k <= kE1 + 6 * 3 && (k - kE1) % 6 == 0) {
+            weight2(sc0, ic<8 + 2 * ((k - kE1) / 6)>{});
+            if constexpr (k == kE1 + 6 * 3) {
+              pop[1] = __builtin_bit_cast(bf16x8, (u32x4){pk[4], pk[5], pk[6], pk[7]});
+              fold_ls();
+            }
+          } else if constexpr (k >= kM1 && k < kM1 + 5) {
+            // the last score MFMA went out one slot before: let its result land
+            if constexpr (k == kM1) {
+              asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+              MLA_SB();  // (reads of sc1 stay below the wait states)
+            }
+            max_part(sc1, ic<k - kM1>{});
+          } else if constexpr (k >= kW1) {
+            weight2(sc1, ic<2 * (k - kW1)>{});
           }
         };
-        auto hook_s1f = [&](auto g) {
-          hook_s1(g);
-          if constexpr (decltype(g)::value == 1) decide();
-        };
-        score_tile<32 * 128>(sc1, ka, qreg, hook_s1f, pay_s1);
-
-        bf16x8 pop[2];
-        pop[0] = __builtin_bit_cast(bf16x8, (u32x4){pk[0], pk[1], pk[2], pk[3]});
-        pop[1] = __builtin_bit_cast(bf16x8, (u32x4){pk[4], pk[5], pk[6], pk[7]});
-        auto pay_pv0 = [&](auto slot) {
-          if constexpr (decltype(slot)::value <= 4) max_slots(sc1, slot);
-        };
-        pv_tile<0>(oacc, pop, va, hook_pv0, pay_pv0);
-
-        decide();
+        auto hook_c = [&](auto slot) {
+          constexpr int k = decltype(slot)::value;
+          if constexpr (k == kE0 - 1) {
+            need = m_tile > m_run + kTau;
+            if (__any(need)) rescale();
+            neg_m = -m_run;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sc1[i], c_log2, neg_m));
-          ls[i & 3] += pv;
-          pf[i & 1] = pv;
-          if (i & 1)
-            pk[i >> 1] = __builtin_bit_cast(uint32_t,
-                                            __builtin_convertvector((f32x2){pf[0], pf[1]}, bf16x2));
+            for (int j = 0; j < 4; ++j) ls[j] = 0.f;
+          } else if constexpr (k == kW1 - 1) {
+            need = m_tile > m_run + kTau;
+          } else if constexpr (!FP8 && k >= kLd && k <= kLd + 3 * 8 && (k - kLd) % 3 == 0) {
+            load(ic<9 + (k - kLd) / 3>{});
+          }
+        };
+        combined_chain(sc1, oacc, pop, qreg, ka, va, hook_c, pay_c);
+        if (__any(need)) {
+          // the running max moves for tile 1: rescale (the chain has drained)
+          // and redo the weights of keys 0..7 under the new max
+          rescale();
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ls[j] = 0.f;
+          weight2(sc1, ic<0>{});
+          weight2(sc1, ic<2>{});
+          weight2(sc1, ic<4>{});
+          weight2(sc1, ic<6>{});
         }
         pop[0] = __builtin_bit_cast(bf16x8, (u32x4){pk[0], pk[1], pk[2], pk[3]});
-        // weights of keys 16..31 at every other slot of groups 0..3 (used from
-        // group 4 on)
+        // weights of keys 16..31 in slots 0, 4, 8, 12 (used from MFMA 16 on)
         auto pay_pv1 = [&](auto slot) {
           constexpr int k = decltype(slot)::value;
-          if constexpr (k < 16 && k % 2 == 0) {
-            weight(sc1, ic<k / 2 + 8>{}, pf);
-            if constexpr (k == 14)
+          if constexpr (k < 16 && k % 4 == 0) {
+            weight2(sc1, ic<k / 2 + 8>{});
+            if constexpr (k == 12)
               pop[1] = __builtin_bit_cast(bf16x8, (u32x4){pk[4], pk[5], pk[6], pk[7]});
-          } else if constexpr (k == 15) {
-            l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-            pin(l_run);
+          } else if constexpr (k == 13) {
+            fold_ls();
           }
         };
         pv_tile<1>(oacc, pop, va, no_hook, pay_pv1);

@@ -7,6 +7,17 @@ know those registers are being written in the background.  This test walks
 each kernel's instruction stream and checks that no instruction touches a
 register of a read that is still in flight: LDS reads complete in order, so
 after lgkmcnt(N) every LDS read except the newest N has landed.
+
+The MFMAs are inline assembly too, so the compiler's hazard recognizer does
+not see them either; the walk also checks the two MFMA data hazards the
+kernel has to cover by hand (counted in wait states: one per instruction,
+N + 1 for s_nop N):
+  * a VALU write of a register an MFMA then reads needs 2 wait states;
+  * an MFMA result read or overwritten by anything but the next MFMA of the
+    same accumulation needs 12 (what the compiler itself inserts after a
+    32x32x16 MFMA on gfx950).
+The walk follows the code in layout order, which for these straight-line
+chains is execution order.
 """
 
 import os
@@ -85,6 +96,52 @@ def _check(instrs):
     return bad
 
 
+def _split(ins):
+    op = ins.split()[0]
+    return op, [o.strip() for o in ins[len(op):].split(",")]
+
+
+def _wait_states(ins):
+    op, args = _split(ins)
+    return int(args[0], 0) + 1 if op == "s_nop" else 1
+
+
+VALU_TO_MFMA = 2
+MFMA_TO_OTHER = 12
+
+
+def _mfma_hazards(instrs):
+    bad = []
+    for i, ins in enumerate(instrs):
+        op, args = _split(ins)
+        if not op.startswith("v_mfma"):
+            continue
+        # (1) VALU writes of the sources shortly before
+        srcs = set().union(*(_regs(a) for a in args[1:4]))
+        ws, j = 0, i - 1
+        while j >= 0 and ws < VALU_TO_MFMA:
+            pop, pargs = _split(instrs[j])
+            if pop.startswith("v_") and not pop.startswith("v_mfma") and pargs and \
+                    _regs(pargs[0]) & srcs:
+                bad.append((i, ins, instrs[j]))
+            ws += _wait_states(instrs[j])
+            j -= 1
+        # (2) uses of the result shortly after
+        dst = _regs(args[0])
+        ws, j = 0, i + 1
+        while j < len(instrs) and ws < MFMA_TO_OTHER:
+            nop, nargs = _split(instrs[j])
+            if nop.startswith("v_mfma"):
+                same_acc = len(nargs) > 3 and _regs(nargs[3]) == dst and _regs(nargs[0]) == dst
+                if not same_acc and dst & set().union(*(_regs(a) for a in nargs)):
+                    bad.append((i, ins, instrs[j]))
+            elif nop != "s_nop" and dst & _regs(instrs[j][len(nop):]):
+                bad.append((i, ins, instrs[j]))
+            ws += _wait_states(instrs[j])
+            j += 1
+    return bad
+
+
 @pytest.fixture(scope="module")
 def decode_asm():
     if not os.path.exists(HIPCC):
@@ -120,3 +177,22 @@ def test_checker_flags_a_planted_use():
     assert _check(good) == []
     assert len(_check(bad)) == 1
     assert [i for i, _ in _check(partial)] == [4]
+
+
+def test_no_unguarded_mfma_hazard(decode_asm):
+    for name, instrs in _kernels(decode_asm).items():
+        bad = _mfma_hazards(instrs)
+        assert not bad, f"{name}: {len(bad)} MFMA hazards, e.g. {bad[:3]}"
+
+
+def test_hazard_walk_flags_planted_cases():
+    mf = "v_mfma_f32_32x32x16_bf16 a[0:15], v[4:7], v[8:11], a[0:15]"
+    mf2 = "v_mfma_f32_32x32x16_bf16 a[0:15], v[12:15], v[8:11], a[0:15]"
+    assert _mfma_hazards(["v_mov_b32_e32 v5, v1", mf]) != []
+    assert _mfma_hazards(["v_mov_b32_e32 v5, v1", "s_nop 1", mf]) == []
+    assert _mfma_hazards(["v_mov_b32_e32 v5, v1", "s_nop 0", mf]) != []
+    assert _mfma_hazards(["v_mov_b32_e32 v30, v1", mf]) == []
+    # accumulation into the same tile right after is fine, a read is not
+    assert _mfma_hazards([mf, mf2]) == []
+    assert _mfma_hazards([mf, "v_accvgpr_read_b32 v1, a3"]) != []
+    assert _mfma_hazards([mf, "s_nop 7", "s_nop 3", "v_accvgpr_read_b32 v1, a3"]) == []
