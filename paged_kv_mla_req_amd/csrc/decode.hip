@@ -79,12 +79,12 @@ constexpr int kLoadsPerPage = kPageBytes / 1024;         // 72 wave-wide 1 KiB l
 constexpr int kLoadsPerWave = kLoadsPerPage / kWaves;    // 18
 constexpr int kKSteps = kD / 16;                         // 36 MFMA k-steps for S
 constexpr int kVTiles = kDv / 32;                        // 16 output tiles of 32 columns
-constexpr float kTau = 8.0f;
-// The page loop issues the next page's loads one per MFMA block: after the 9
-// score blocks and 8 output blocks of the first tile, and the first score
-// block of the second (bf16: 18 loads; e4m3: 9, all in the first score tile).
+constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
+// The page loop issues the next page's loads one per block of four MFMAs of
+// the first score tile (e4m3: all 9; bf16: 9 of 18), the rest of bf16 one
+// every third slot early in the second tile's chain.
 static_assert(kLoadsPerWave == 18 && kLoadsPerWaveF8 == 9 && kKSteps / 4 == 9,
-              "load spreading assumes 18 / 9 loads and 9 score blocks");                             // lazy-rescale threshold (log2 units)
+              "load spreading assumes 18 / 9 loads and 9 score blocks");
 
 // Scalar arguments of the decode kernel (pointers are kernel arguments of
 // their own, marked __restrict__, so the compiler may read the small index
@@ -948,37 +948,44 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
       constexpr bool MASKED = decltype(masked_c)::value;
       __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of page `it` landed
       __syncthreads();                     // ... and every wave's; buffer it+1 is free again
-      const lds_u8* base = LDS_PTR(uint8_t, smem) + (FP8 ? 0 : (it & 1) * kPageBytes);
-      // The next page's loads are issued one per MFMA block (see above):
-      // issued back to back they would stall the wave until the address unit
-      // drains them.
-      const bool has_next = it + 1 < total;
-      const __amdgpu_buffer_rsrc_t next_rsrc =
-          page_rsrc<FP8 ? kD : kRowBytes>(kv + nphys() * kSrcPageBytes,
-                                           __builtin_amdgcn_readfirstlane(nrows));
-      uint8_t* const next_buf = FP8 ? smem + kPageBytes + ((it + 1) & 1) * kPageBytesF8
-                                    : smem + ((it + 1) & 1) * kPageBytes;
-      // The cursor moves on to page it + 2 now: its block-table entry then has
-      // this whole page to arrive.
-      if (it + 1 < total) advance();
       const uint32_t plane = pinned_lane();
       const LaneOffsets lo = lane_offsets(plane, wave);
+      const lds_u8* base = LDS_PTR(uint8_t, smem) + (FP8 ? 0 : (it & 1) * kPageBytes);
+      // The next page's loads are spread over the MFMA work (issued back to
+      // back they would stall the wave until the address unit drains them).
+      // Their range and the cursor's step to page it + 2 (whose block-table
+      // entry then has this whole page to arrive) are worked out in the shadow
+      // of the first MFMAs.  After the part's last page the loads still go out, over an
+      // empty range: they only write zeros into the free buffer (and cost no
+      // branch per load); the kernel waits for them before it ends.
+      const bool has_next = it + 1 < total;
+      __amdgpu_buffer_rsrc_t next_rsrc;
+      uint8_t* const next_buf = FP8 ? smem + kPageBytes + ((it + 1) & 1) * kPageBytesF8
+                                    : smem + ((it + 1) & 1) * kPageBytes;
+      auto start_next = [&]() {
+        next_rsrc = page_rsrc<FP8 ? kD : kRowBytes>(
+            kv + nphys() * kSrcPageBytes, has_next ? __builtin_amdgcn_readfirstlane(nrows) : 0);
+        if (has_next) advance();
+      };
       // load K of this wave's share, K < 18 (bf16) or K < 9 (e4m3)
       auto load = [&](auto kc) {
         constexpr int K = decltype(kc)::value;
-        if (has_next) {
-          if constexpr (FP8)
-            issue_one_load_f8<K>(next_rsrc, next_buf, wave, wave * 1024 + 16 * plane);
-          else
-            issue_one_load<K>(next_rsrc, next_buf, wave, lo.load, lo.load + 4 * (8 * kRowBytes));
-        }
+        if constexpr (FP8)
+          issue_one_load_f8<K>(next_rsrc, next_buf, wave, wave * 1024 + 16 * plane);
+        else
+          issue_one_load<K>(next_rsrc, next_buf, wave, lo.load, lo.load + 4 * (8 * kRowBytes));
       };
-      auto hook_s0 = [&](auto g) { load(g); };
+      auto hook_s0 = [&](auto g) {
+        constexpr int G = decltype(g)::value;
+        if constexpr (G == 0) start_next();
+        load(ic<G>{});
+      };
+      // bf16 loads 9..17, where the masked path issues them
       auto hook_pv0 = [&](auto b) {
-        if constexpr (!FP8) load(std::integral_constant<int, 9 + decltype(b)::value>{});
+        if constexpr (!FP8) load(ic<9 + decltype(b)::value>{});
       };
       auto hook_s1 = [&](auto g) {
-        if constexpr (!FP8 && decltype(g)::value == 0) load(std::integral_constant<int, 17>{});
+        if constexpr (!FP8 && decltype(g)::value == 0) load(ic<17>{});
       };
       auto no_hook = [](auto) {};
       if constexpr (FP8) {
@@ -1056,7 +1063,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
         // payload slots of the combined chain
         constexpr int kE0 = 5;                 // tile 0, keys 0..7: slots 5..8
         constexpr int kE1 = kCPrefix + 1;      // tile 0, keys 8..15: slots 10, 16, 22, 28
-        constexpr int kLd = kCPrefix + 2;      // next-page loads 9..17: slots 11, 14, .., 35
+        constexpr int kLd = kCPrefix + 2;      // bf16 loads 9..17: slots 11, 14, .., 35
         constexpr int kM1 = kCLastScore + 1;   // max(1): slots 59..63
         constexpr int kW1 = kM1 + 5;           // tile 1, keys 0..7: slots 64..67
         static_assert(kE0 + 4 == kCPrefix && kCPrefix == kCFirstOut && kE1 + 6 * 3 < kCOutU1 &&
@@ -1242,6 +1249,8 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
     __syncthreads();
     if constexpr (FP8) __syncthreads();
   }
+  // the last page's empty loads land before the work-group's LDS is released
+  __builtin_amdgcn_s_waitcnt(0x0f70);
 }
 
 }  // namespace mla
