@@ -62,6 +62,7 @@ typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
@@ -739,55 +740,71 @@ __device__ __forceinline__ LaneOffsets lane_offsets(uint32_t lane, int wave) {
 // buffers, so no other wave is ever waiting on them).
 constexpr int kStageBytes = 4096;
 
-// Write this wave's 32 rows of o * scale, as rows of 512 values, to dst
-// (row r of the request at dst + r * 512; rows >= rows are skipped), in
-// bf16 (T = uint16_t) or fp32 (T = float).  The accumulators hold O^T
-// (lane (n, h): row n, 16 values per tile), so direct stores would write
-// 8- or 16-byte pieces of 32 rows per instruction.  Instead the rows pass
-// through the wave's own LDS area, 128 bytes of each row at a time (the
-// 16-byte chunk c of row n sits at c ^ (n % 8), which spreads both the
-// writes and the reads over the banks), and leave as whole 128-byte row
-// segments, 8 rows per store instruction.
-template <typename T>
+// Values 4G .. 4G+3 of an accumulator tile to LDS, straight from the
+// accumulator registers.
+template <int G>
+__device__ __forceinline__ void stage_quad(const f32x16& tile, uint32_t addr) {
+  const f32x4 quad = __builtin_shufflevector(tile, tile, 4 * G, 4 * G + 1, 4 * G + 2, 4 * G + 3);
+  asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "a"(quad) : "memory");
+}
+
+// Write this wave's 32 rows of o * scale, as rows of 512 values, to dst (row
+// r at dst + r * 512), in fp32 (T = float: the partial state of a piece) or
+// bf16 (T = uint16_t: the output of an unsplit request).  The accumulators
+// hold O^T (lane (n, h): row n, 16 values per tile), so direct stores would
+// write 16-byte pieces of 32 rows per instruction.  Instead each tile (32
+// columns, 128 bytes of each row in fp32) goes to the wave's own LDS area
+// straight from the accumulator registers, unscaled (the 16-byte chunk c of
+// row n at c ^ (n % 8), which spreads writes and reads over the banks), and
+// leaves row-major: lane i reads 4 values of row 8 qq + i / 8, scales them by
+// that row's scale (taken from the lane that computed it) and stores them,
+// so that a store instruction covers 8 rows x 128 bytes (fp32) or 64 bytes
+// (bf16).  Few registers are live at a time, which leaves the next piece's
+// queries room to stay in registers across the epilogue.  FULL: all 32 rows
+// exist (no row checks).
+template <typename T, bool FULL>
 __device__ __forceinline__ void store_rows(const f32x16 (&oacc)[kVTiles], float scale,
                                            uint8_t* stage, T* dst, int row0, int rows,
                                            uint32_t lane) {
   constexpr bool kBf16 = sizeof(T) == 2;
-  constexpr int kTiles = kBf16 ? 2 : 1;  // accumulator tiles per 128-byte row segment
-  constexpr int kCols = 32 * kTiles;     // columns per pass
-  const int n = lane & 31, h = lane >> 5;
+  const int n = lane & 31, h = lane >> 5, j = lane & 7;
+  const uint32_t sbase = (uint32_t)(uintptr_t)LDS_PTR(uint8_t, stage);
+  uint32_t wa[4];  // LDS addresses of this lane's 4 chunks of a tile (chunk 2g + h of row n)
 #pragma unroll
-  for (int p = 0; p < kVTiles / kTiles; ++p) {
+  for (int g = 0; g < 4; ++g) wa[g] = sbase + n * 128 + (((2 * g + h) ^ (n & 7)) << 4);
+  float rs[4];
+  T* rowp[4];
+  const uint4* ra[4];
 #pragma unroll
-    for (int t = 0; t < kTiles; ++t)
+  for (int qq = 0; qq < 4; ++qq) {
+    const int row = 8 * qq + (int)(lane >> 3);
+    rs[qq] = __shfl(scale, row);
+    ra[qq] = reinterpret_cast<const uint4*>(stage + row * 128 + ((j ^ (row & 7)) << 4));
+    rowp[qq] = dst + (int64_t)(row0 + row) * kDv + 4 * j;
+  }
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        // this lane's 4 values: columns 32 (kTiles p + t) + 8 g + 4 h .. +3
-        const f32x16& o = oacc[kTiles * p + t];
-        const float v0 = o[4 * g] * scale, v1 = o[4 * g + 1] * scale;
-        const float v2 = o[4 * g + 2] * scale, v3 = o[4 * g + 3] * scale;
-        if constexpr (kBf16) {
-          const int c = 4 * t + g;  // 16-byte chunk (8 columns); this lane has half
-          const uint32_t lo =
-              __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){v0, v1}, bf16x2));
-          const uint32_t hi =
-              __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){v2, v3}, bf16x2));
-          *reinterpret_cast<uint2*>(stage + n * 128 + ((c ^ (n & 7)) << 4) + 8 * h) =
-              make_uint2(lo, hi);
-        } else {
-          const int c = 2 * g + h;  // 16-byte chunk (4 columns), all this lane's
-          *reinterpret_cast<float4*>(stage + n * 128 + ((c ^ (n & 7)) << 4)) =
-              make_float4(v0, v1, v2, v3);
-        }
-      }
+  for (int p = 0; p < kVTiles; ++p) {
+    stage_quad<0>(oacc[p], wa[0]);
+    stage_quad<1>(oacc[p], wa[1]);
+    stage_quad<2>(oacc[p], wa[2]);
+    stage_quad<3>(oacc[p], wa[3]);
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
-      const int row = 8 * qq + (int)(lane >> 3), j = lane & 7;
-      const uint4 v = *reinterpret_cast<const uint4*>(stage + row * 128 + ((j ^ (row & 7)) << 4));
-      if (row0 + row < rows)
-        *reinterpret_cast<uint4*>(dst + (int64_t)(row0 + row) * kDv + kCols * p +
-                                  j * (16 / (int)sizeof(T))) = v;
+      const float4 v = __builtin_bit_cast(float4, *ra[qq]);
+      const float x0 = v.x * rs[qq], x1 = v.y * rs[qq], x2 = v.z * rs[qq], x3 = v.w * rs[qq];
+      if (FULL || row0 + 8 * qq + (int)(lane >> 3) < rows) {
+        if constexpr (kBf16) {
+          const uint32_t lo =
+              __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x0, x1}, bf16x2));
+          const uint32_t hi =
+              __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x2, x3}, bf16x2));
+          *reinterpret_cast<uint2*>(rowp[qq] + 32 * p) = make_uint2(lo, hi);
+        } else {
+          *reinterpret_cast<float4*>(rowp[qq] + 32 * p) = make_float4(x0, x1, x2, x3);
+        }
+      }
     }
+    __builtin_amdgcn_sched_barrier(0);  // one tile of registers live at a time
   }
 }
 
@@ -904,10 +921,32 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
 
   bf16x8 qreg[kKSteps];
   f32x16 oacc[kVTiles];
+  // Query rows of request b into qreg.  A lane whose row is past the last one
+  // reads row 0 instead: its results stay in that lane's row of the
+  // accumulators and are never stored, so no select on the loaded values
+  // makes the wave wait for them where they are loaded.
+  auto load_q = [&](int b) {
+    const uint32_t ql = pinned_lane();
+    const int r = row0 + (int)(ql & 31);
+    const uint16_t* qrow =
+        q + ((int64_t)b * P.rows + (r < P.rows ? r : 0)) * kD + 8 * (int)(ql >> 5);
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 16 * ks);
+      if (FP8) v ^= q_sign;
+      qreg[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  };
   int it = 0;  // pages of this part processed so far (selects the LDS buffer)
   int cb = b_first;
   int cp = pg_first;
   int piece = first_piece;
+  // The queries of a piece after the first are loaded during the previous
+  // piece's last page, once its last score MFMA has read them, and waited
+  // for before that piece's output stores: vector memory operations complete
+  // in order, so queries loaded after the stores would wait for them.
+  bool first_wait = true;
+  load_q(cb);
   while (true) {
     // ---- one piece: pages [cp, cend) of request cb ---------------------------
     const int32_t L = uniform_load(seq_lens, cb);
@@ -916,24 +955,17 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
     const int32_t lim_min = P.causal ? L - P.q_len + i_tok_min : L - 1;
     const int first_masked =
         __builtin_amdgcn_readfirstlane(lim_min >= 0 ? (lim_min + 1) / kPage : 0);
-    {
-      // A lane whose row is past the last one reads row 0 instead: its results
-      // stay in that lane's row of the accumulators and are never stored, so
-      // (bf16) no select on the loaded values makes the wave wait for them here.
-      const uint32_t ql = pinned_lane();
-      const int r = row0 + (int)(ql & 31);
-      const uint16_t* qrow =
-          q + ((int64_t)cb * P.rows + (r < P.rows ? r : 0)) * kD + 8 * (int)(ql >> 5);
-#pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) {
-        u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 16 * ks);
-        if (FP8) v ^= q_sign;
-        // (the e4m3 kernel keeps the select: without it the compiler spills an
-        // accumulator tile around the epilogue)
-        if (FP8 && !(r < P.rows)) v = (u32x4){0, 0, 0, 0};
-        qreg[ks] = __builtin_bit_cast(bf16x8, v);
-      }
+    // the part's next request that has pages (if the part goes on past this one)
+    int ncb = cb;
+    if (cb < b_last) {
+      do {
+        ++ncb;
+      } while (ncb < b_last && page_count(uniform_load(seq_lens, ncb)) <= 0);
     }
+    // on the piece's last page, if another piece follows: load its queries
+    auto prefetch_q = [&]() {
+      if (cp + 1 == cend && it + 1 < total && cb < b_last) load_q(ncb);
+    };
 #pragma unroll
     for (int vt = 0; vt < kVTiles; ++vt) oacc[vt] = (f32x16){};
     float m_run = -INFINITY, l_run = 0.f;
@@ -946,8 +978,12 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
     // registers in place.
     auto page = [&](auto masked_c) {
       constexpr bool MASKED = decltype(masked_c)::value;
-      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of page `it` landed
-      __syncthreads();                     // ... and every wave's; buffer it+1 is free again
+      // vmcnt(0): this wave's loads of page `it` landed (for a piece's first
+      // page after the first piece: waited for before the previous epilogue);
+      // the barrier: every wave's, and buffer it+1 is free again
+      if (first_wait) __builtin_amdgcn_s_waitcnt(0x0f70);
+      first_wait = true;
+      __syncthreads();
       const uint32_t plane = pinned_lane();
       const LaneOffsets lo = lane_offsets(plane, wave);
       const lds_u8* base = LDS_PTR(uint8_t, smem) + (FP8 ? 0 : (it & 1) * kPageBytes);
@@ -1109,6 +1145,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
           }
         };
         combined_chain(sc1, oacc, pop, qreg, ka, va, hook_c, pay_c);
+        prefetch_q();
         if (__any(need)) {
           // the running max moves for tile 1: rescale (the chain has drained)
           // and redo the weights of keys 0..7 under the new max
@@ -1142,10 +1179,12 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
         for (int t = 0; t < 2; ++t) {
           // ---- S^T = K Q^T for 32-key tile t; sc[i] is key 32t + 16h + i -----------
           f32x16 sc;
-          if (t == 0)
+          if (t == 0) {
             score_tile<0>(sc, ka, qreg, hook_s0, NoSlot{});
-          else
+          } else {
             score_tile<32 * 128>(sc, ka, qreg, hook_s1, NoSlot{});
+            prefetch_q();
+          }
           // ---- row max of the scaled scores; weights p = 2^(c s - m) -----------------
           // c = softmax_scale * log2(e) > 0, so max(c s) = c max(s).  Keys a row
           // cannot see (causal limit, page tail) are excluded on the pages
@@ -1214,6 +1253,12 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
     for (; cp < cend && it < total; ++cp, ++it) page(std::true_type{});
 
     // ---- epilogue of the piece ---------------------------------------------------
+    const bool more = it < total && cb < b_last;
+    if (more) {
+      // the next piece's queries and first page land before any store goes out
+      __builtin_amdgcn_s_waitcnt(0x0f70);
+      first_wait = false;
+    }
     {
       const float l_tot = xhalf_sum(l_run);
       const float inv = l_tot > 0.f ? delta / l_tot : 0.f;
@@ -1229,17 +1274,22 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
       const int r = row0 + (int)(ln & 31);
       if (to_partial && slot < P.partial_slots) {
         if ((ln >> 5) == 0 && r < P.rows) partial_lse[slot * P.rows + r] = lse_val;
-        store_rows(oacc, inv, stage_all[wave], partial_o + slot * P.rows * kDv, row0, P.rows, ln);
+        float* const po = partial_o + slot * P.rows * kDv;
+        if (row0 + kRowsPerWave <= P.rows)
+          store_rows<float, true>(oacc, inv, stage_all[wave], po, row0, P.rows, ln);
+        else
+          store_rows<float, false>(oacc, inv, stage_all[wave], po, row0, P.rows, ln);
       } else if (!to_partial) {
         if (lse_out && (ln >> 5) == 0 && r < P.rows) lse_out[(int64_t)cb * P.rows + r] = lse_val;
-        store_rows(oacc, inv, stage_all[wave], out + (int64_t)cb * P.rows * kDv, row0, P.rows, ln);
+        uint16_t* const ob = out + (int64_t)cb * P.rows * kDv;
+        if (row0 + kRowsPerWave <= P.rows)
+          store_rows<uint16_t, true>(oacc, inv, stage_all[wave], ob, row0, P.rows, ln);
+        else
+          store_rows<uint16_t, false>(oacc, inv, stage_all[wave], ob, row0, P.rows, ln);
       }
     }
-    if (it >= total || cb >= b_last) break;
-    // next request of the part that has pages
-    do {
-      ++cb;
-    } while (cb < b_last && page_count(uniform_load(seq_lens, cb)) <= 0);
+    if (!more) break;
+    cb = ncb;
     cp = 0;
     piece = 0;
   }
