@@ -112,7 +112,7 @@ mla_status mla_build_block_table(const int32_t* req_to_token, int32_t r2t_rows,
  *
  * Rule (deterministic, depends only on seq_lens, rows_per_req, num_parts),
  * in quarter pages: request b has N_b = ceil(L_b/64) pages and costs
- * 4 N_b + c, with c = 4 + ceil(10 rows_per_req / 128) the per-piece overhead
+ * 4 N_b + c, with c = 4 + ceil(8 rows_per_req / 128) the per-piece overhead
  * (0 for an empty request).  With C the total cost, part p covers cost
  * positions [floor(pC/P), floor((p+1)C/P)); a position x inside request b
  * maps to the page boundary clamp(floor((x - cum_b - c + 2) / 4), 0, N_b).

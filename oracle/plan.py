@@ -38,9 +38,10 @@ PAGE_SIZE = 64
 
 def plan_overhead(rows_per_req: int) -> int:
     """Fixed per-piece cost in quarter pages: loading q and writing the
-    result of ``rows_per_req`` rows, plus one page.  (A measured choice of
-    this library: a 128-row piece costs about 3.4 pages of work.)"""
-    return 4 + (10 * rows_per_req + 127) // 128
+    result of ``rows_per_req`` rows (and the waits these cause), plus one
+    page.  (A measured choice of this library: a 128-row piece costs about
+    3 pages of work.)"""
+    return 4 + (8 * rows_per_req + 127) // 128
 
 
 def _locate(g: int, pagecum: np.ndarray, npages: np.ndarray):

@@ -916,7 +916,10 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
   // Per-tensor dequantisation scale: scores use |delta| in the softmax scale
   // and the sign on q; the output is multiplied by delta.
   const float delta = FP8 ? kv_descale[0] : 1.0f;
-  const float c_log2 = P.scale_log2 * fabsf(delta);
+  // (kept above 0 so that a masked score, -inf, scales to -inf and never to
+  // 0 * inf; a zero scale then weights the visible keys equally, to within
+  // 1e-30 of a relative error)
+  const float c_log2 = fmaxf(P.scale_log2 * fabsf(delta), 1e-30f);
   const uint32_t q_sign = (FP8 && delta < 0.f) ? 0x80008000u : 0u;
 
   bf16x8 qreg[kKSteps];
@@ -971,11 +974,10 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
     float m_run = -INFINITY, l_run = 0.f;
 
     // One page of the piece.  MASKED: some key of the page may be invisible to
-    // some row of the wave (page tail, causal limit); those pages (at most
-    // the last one or, for several tokens per request, the last few) run
-    // one tile at a time with explicit masking.  The two kinds run as two
-    // loops rather than a branch inside one, which keeps the 256 output
-    // registers in place.
+    // some row of the wave (page tail, causal limit); on those pages (at most
+    // the last one or, for several tokens per request, the last few) the
+    // scores of such keys are masked before the softmax.  The two kinds are
+    // two instances of the same code, run as two loops.
     auto page = [&](auto masked_c) {
       constexpr bool MASKED = decltype(masked_c)::value;
       // vmcnt(0): this wave's loads of page `it` landed (for a piece's first
@@ -1016,13 +1018,6 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
         if constexpr (G == 0) start_next();
         load(ic<G>{});
       };
-      // bf16 loads 9..17, where the masked path issues them
-      auto hook_pv0 = [&](auto b) {
-        if constexpr (!FP8) load(ic<9 + decltype(b)::value>{});
-      };
-      auto hook_s1 = [&](auto g) {
-        if constexpr (!FP8 && decltype(g)::value == 0) load(ic<17>{});
-      };
       auto no_hook = [](auto) {};
       if constexpr (FP8) {
         convert_f8_page(smem + kPageBytes + (it & 1) * kPageBytesF8, smem, wave);
@@ -1033,8 +1028,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
       const uint32_t pbase = (uint32_t)(uintptr_t)base;
       const uint32_t ka = pbase + lo.k, va = pbase + lo.v;
 
-      if constexpr (!MASKED) {
-        // ---- no key of this page is masked for any row of the wave ----------------
+      {
         // The softmax of each tile runs in the shadow of the matrix work:
         //   S(0)
         //   S(1) + PV(0) mixed | max(0), rescale decision, weights P(0);
@@ -1042,8 +1036,22 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
         //                        under the running max as it stands
         //   (rare: the running max moves for tile 1 -> rescale, redo those weights)
         //   PV(1) | weights P(1) for keys 16..31 (used from group 4 on)
-        // sc0[i] / sc1[i] is key 16h + i of tile 0 / 1.
+        // sc0[i] / sc1[i] is key 16h + i of tile 0 / 1.  On a MASKED page the
+        // scores of keys a row cannot see are set to -inf before the row max
+        // (weights 2^-inf = 0).
         f32x16 sc0, sc1;
+        int vis0 = 16, vis1 = 16;  // elements i < vis of the lane's 16 are visible keys
+        if constexpr (MASKED) {
+          const int r = row0 + (int)(plane & 31);
+          const int i_tok = r < P.rows ? r / P.heads : 0;
+          const int32_t lim = P.causal ? L - P.q_len + i_tok : L - 1;  // last visible key
+          vis0 = lim - (cp * kPage + 16 * (int)(plane >> 5)) + 1;
+          vis1 = vis0 - 32;
+        }
+        auto mask_tile = [&](f32x16& sc, int vis) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sc[i] = i < vis ? sc[i] : -INFINITY;
+        };
         score_tile<0>(sc0, ka, qreg, hook_s0, NoSlot{});
 
         float mx[4], ls[4];
@@ -1093,7 +1101,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
             for (int vt = 0; vt < kVTiles; ++vt) scale_tile(oacc[vt], alpha);
           }
           m_run = m_new;
-          neg_m = -m_run;  // finite: this tile has a finite max
+          neg_m = m_run == -INFINITY ? 0.f : -m_run;  // -inf: no visible key yet
         };
         bf16x8 pop[2];
         // payload slots of the combined chain
@@ -1108,6 +1116,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
         auto pay_c = [&](auto slot) {
           constexpr int k = decltype(slot)::value;
           if constexpr (k < kE0) {
+            if constexpr (MASKED && k == 0) mask_tile(sc0, vis0);
             max_part(sc0, slot);
           } else if constexpr (k < kE0 + 4) {
             weight2(sc0, ic<2 * (k - kE0)>{});
@@ -1124,6 +1133,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
             if constexpr (k == kM1) {
               asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
               MLA_SB();  // (reads of sc1 stay below the wait states)
+              if constexpr (MASKED) mask_tile(sc1, vis1);
             }
             max_part(sc1, ic<k - kM1>{});
           } else if constexpr (k >= kW1) {
@@ -1135,7 +1145,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
           if constexpr (k == kE0 - 1) {
             need = m_tile > m_run + kTau;
             if (__any(need)) rescale();
-            neg_m = -m_run;
+            neg_m = m_run == -INFINITY ? 0.f : -m_run;
 #pragma unroll
             for (int j = 0; j < 4; ++j) ls[j] = 0.f;
           } else if constexpr (k == kW1 - 1) {
@@ -1170,84 +1180,9 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
           }
         };
         pv_tile<1>(oacc, pop, va, no_hook, pay_pv1);
-      } else {
-        // ---- a page where some key may be masked: one tile at a time --------------
-        const int r = row0 + (plane & 31);
-        const int i_tok = r < P.rows ? r / P.heads : 0;
-        const int32_t lim = P.causal ? L - P.q_len + i_tok : L - 1;  // last visible key
-  #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          // ---- S^T = K Q^T for 32-key tile t; sc[i] is key 32t + 16h + i -----------
-          f32x16 sc;
-          if (t == 0) {
-            score_tile<0>(sc, ka, qreg, hook_s0, NoSlot{});
-          } else {
-            score_tile<32 * 128>(sc, ka, qreg, hook_s1, NoSlot{});
-            prefetch_q();
-          }
-          // ---- row max of the scaled scores; weights p = 2^(c s - m) -----------------
-          // c = softmax_scale * log2(e) > 0, so max(c s) = c max(s).  Keys a row
-          // cannot see (causal limit, page tail) are excluded on the pages
-          // where they can occur.
-          const int key0 = cp * kPage + 32 * t + 16 * (int)(plane >> 5);
-          const bool masked = cp >= first_masked;
-          float mx[4];
-          if (masked) {
-  #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              mx[j] = -INFINITY;
-  #pragma unroll
-              for (int i = j; i < 16; i += 4)
-                mx[j] = fmaxf(mx[j], (key0 + i <= lim) ? sc[i] : -INFINITY);
-            }
-          } else {
-  #pragma unroll
-            for (int j = 0; j < 4; ++j)
-              mx[j] = fmaxf(fmaxf(sc[j], sc[j + 4]), fmaxf(sc[j + 8], sc[j + 12]));
-          }
-          const float mloc = xhalf_max(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])));
-          const float m_tile = (mloc == -INFINITY) ? -INFINITY : c_log2 * mloc;
-          const bool need = m_tile > m_run + kTau;
-          if (__any(need)) {
-            const float m_new = need ? m_tile : m_run;
-            const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-            l_run *= alpha;
-            // Rows whose running max is still -inf have o = 0: only a wave with
-            // some earlier weight needs the 256-register rescale.
-            if (__any(need && m_run != -INFINITY)) {
-  #pragma unroll
-              for (int vt = 0; vt < kVTiles; ++vt) scale_tile(oacc[vt], alpha);
-            }
-            m_run = m_new;
-          }
-          const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
-          bf16x8 pop[2];
-          float ls[4] = {0.f, 0.f, 0.f, 0.f};
-          if (masked) {
-  #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const float e = __builtin_amdgcn_exp2f(fmaf(sc[i], c_log2, neg_m));
-              const float p = (key0 + i <= lim) ? e : 0.f;
-              ls[i & 3] += p;
-              pop[i >> 3][i & 7] = (__bf16)p;
-            }
-          } else {
-  #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const float p = __builtin_amdgcn_exp2f(fmaf(sc[i], c_log2, neg_m));
-              ls[i & 3] += p;
-              pop[i >> 3][i & 7] = (__bf16)p;
-            }
-          }
-          l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-          // ---- O^T += V^T P^T ------------------------------------------------------------
-          if (t == 0)
-            pv_tile<0>(oacc, pop, va, hook_pv0, NoSlot{});
-          else
-            pv_tile<1>(oacc, pop, va, no_hook, NoSlot{});
-        }
       }
     };
+
     const int cfast = min(cend, max(cp, first_masked));
     for (; cp < cfast && it < total; ++cp, ++it) page(std::false_type{});
     for (; cp < cend && it < total; ++cp, ++it) page(std::true_type{});

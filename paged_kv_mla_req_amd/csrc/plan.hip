@@ -15,10 +15,12 @@
 namespace mla {
 
 // Per-piece overhead in quarter pages: loading q and writing the result of
-// rows_per_req rows, plus a constant (one page of the work costs 4).  On
-// MI355X a 128-row piece costs about 3.4 pages (measured); the rule gives 3.5.
+// rows_per_req rows (and the waits these cause), plus a constant (one page of
+// the work costs 4).  On MI355X a 128-row piece costs about 3 pages
+// (measured: work-group durations against their pages and pieces); the rule
+// gives 3.
 __host__ __device__ __forceinline__ int plan_overhead_q(int rows_per_req) {
-  return 4 + (10 * rows_per_req + 127) / 128;
+  return 4 + (8 * rows_per_req + 127) / 128;
 }
 
 constexpr int kPlanThreads = 256;
