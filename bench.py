@@ -1,7 +1,8 @@
 """Benchmark of the MLA paged-KV decode hot path on one MI355X.
 
-One step = one pass of the whole path over one batch: build the block table,
-plan the splits, run the split decode, merge the partial states.  The
+One step = one pass of the whole path over one batch: build the block table
+and plan the splits (one launch), run the split decode, merge the partial
+states.  The
 workload is the DeepSeek-V3-shaped decode batch: 64 requests, 128 heads,
 q_len 1, KV lengths uniform in [1024, 8192], bf16 q and latent cache with
 64-token pages scattered in a 2x-oversized pool (synthetic, seeded).
@@ -9,7 +10,10 @@ q_len 1, KV lengths uniform in [1024, 8192], bf16 q and latent cache with
 Printed: one JSON line with KV-read GB/s over the whole step (the headline
 metric), tokens/s, the decode kernel's roofline position (bytes it must move
 per launch / its average launch time, against the 8 TB/s HBM peak) and the
-fp64 CPU oracle timed on the host on the same batch.
+fp64 CPU oracle timed on the host on the same batch.  Beside it: the time of
+decode + merge alone and its KV-read rate (the per-layer part of the step,
+which a model repeats for every layer while the table and plan are built
+once per step), and the time of the table-and-plan launch alone.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3]
                        [--no-cpu-baseline] [--pools P]
@@ -26,6 +30,8 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+EV_EVERY = 5     # timed steps per decode launch that records its own events
+SETTLE_S = 0.3   # default seconds of untimed steps before the warm-up steps
 
 
 def _args():
@@ -38,6 +44,8 @@ def _args():
                     help="independent copies of the KV pool, rotated per step so that the "
                          "256 MB last-level cache cannot serve a step from the previous one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle", type=float, default=SETTLE_S,
+                    help="seconds of untimed steps before the warm-up steps (clock settling)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of the step captured in a HIP graph (measured slower than "
                          "eager launches here: the four launches are not host-bound)")
@@ -205,11 +213,14 @@ def main() -> int:
     out = torch.empty((w.bs, w.q_len, w.heads, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((w.bs, w.q_len, w.heads), dtype=torch.float32, device="cuda")
     max_len = int(w.seq_lens.max())
-    # Per timed step, a pair of events that the decode kernel's own launch
-    # records at its begin and end (mla_decode_time_next_launch).  They are
-    # created, and recorded once so that they exist, before timing starts.
+    # For every EV_EVERY-th timed step, a pair of events that the decode
+    # kernel's own launch records at its begin and end
+    # (mla_decode_time_next_launch).  An event-recorded launch ends with a
+    # release to system scope (an L2 write-back), which costs that step a few
+    # microseconds, so only a sample of the timed launches records them.  They
+    # are created, and recorded once so that they exist, before timing starts.
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(a.steps)]
+          for _ in range((a.steps + EV_EVERY - 1) // EV_EVERY)]
     for e0, e1 in ev:
         e0.record()
         e1.record()
@@ -219,16 +230,29 @@ def main() -> int:
                        partial_o=po, partial_lse=pl, out=out, lse=lse, kv_dtype=w.kv_dtype,
                        kv_descale=p.kv_descale, causal=w.causal)
 
+    def table_and_plan(p):
+        mla.build_table_and_plan(p.req_to_token, p.req_pool_indices, p.seq_lens, width, R,
+                                 num_parts, w.kv_dtype, max_seq_len_hint=max_len, out=bt,
+                                 tile_plan=tile_plan, split_indptr=split_indptr)
+
     def step(i: int, timed: int):
+        # one pass of the hot path: block table + plan (one launch), split
+        # decode, merge
         p = pools[i % len(pools)]
-        mla.build_block_table(p.req_to_token, p.req_pool_indices, p.seq_lens, width,
-                              max_seq_len_hint=max_len, out=bt)
-        mla.plan_splits(p.seq_lens, R, num_parts, w.kv_dtype, tile_plan=tile_plan,
-                        split_indptr=split_indptr)
-        if timed >= 0:
-            mla.time_next_decode(*ev[timed])
+        table_and_plan(p)
+        if timed >= 0 and timed % EV_EVERY == 0:
+            mla.time_next_decode(*ev[timed // EV_EVERY])
         decode(p)
         mla.merge_states(po, pl, split_indptr, out, lse)
+
+    def timed_loop(fn, n: int) -> float:
+        """ms per call of fn(i) over n back-to-back calls."""
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for i in range(n):
+            fn(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) * 1e3 / n
 
     if a.calib_copy_mib > 0:
         n = a.calib_copy_mib << 18  # int32 elements
@@ -238,13 +262,24 @@ def main() -> int:
         torch.bitwise_not(src, out=dst)  # reads and writes calib_copy_mib MiB
         torch.cuda.synchronize()
         del src, dst
-    print(f"[bench] warmup {a.warmup} steps", file=sys.stderr, flush=True)
+    # The card raises its clocks over the first ~0.1 s of sustained load: steps
+    # run untimed for SETTLE_S seconds first, then the W warm-up steps.
+    t_settle = time.perf_counter()
+    n_settle = 0
+    while time.perf_counter() - t_settle < a.settle:
+        step(n_settle, -1)
+        n_settle += 1
+        if n_settle % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    print(f"[bench] clock settling: {n_settle} untimed steps; warmup {a.warmup} steps",
+          file=sys.stderr, flush=True)
     for i in range(a.warmup):
         step(i, -1)
     torch.cuda.synchronize()
     graphs = []
     if a.graph:
-        # One captured step per KV pool: the four kernels of the step replay
+        # One captured step per KV pool: the three kernels of the step replay
         # without host launch work between them.
         for j in range(len(pools)):
             g = torch.cuda.CUDAGraph()
@@ -277,6 +312,12 @@ def main() -> int:
         ms_step_eager = (time.perf_counter() - t1) * 1e3 / a.steps
     # the decode kernel's average launch duration over the event-timed steps
     dec_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    # The step's parts on their own (the table and plan run once per batch
+    # step, decode and merge once per attention layer): same inputs, timed
+    # back to back after the main loop.
+    ms_dm = timed_loop(lambda i: (decode(pools[i % len(pools)]),
+                                  mla.merge_states(po, pl, split_indptr, out, lse)), a.steps)
+    ms_tp = timed_loop(lambda i: table_and_plan(pools[i % len(pools)]), a.steps)
 
     b = _algorithmic_bytes(w)
     kv_gbs = b["kv"] / (ms_step * 1e-3) / 1e9
@@ -310,6 +351,9 @@ def main() -> int:
         "pct_hbm_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(tokens_s, 1),
         "decode_kernel_ms": round(dec_ms, 5),
+        "ms_decode_merge": round(ms_dm, 5),
+        "kv_read_gbs_decode_merge": round(b["kv"] / (ms_dm * 1e-3) / 1e9, 2),
+        "ms_table_and_plan": round(ms_tp, 5),
         "step_launch": "hip graph replay" if a.graph else "eager",
         "ms_per_step_eager": None if ms_step_eager is None else round(ms_step_eager, 5),
         "roofline": {

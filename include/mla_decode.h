@@ -139,6 +139,27 @@ mla_status mla_plan_splits(const int32_t* seq_lens, int32_t bs, int32_t rows_per
                            int32_t num_parts, int32_t kv_dtype, int32_t* tile_plan,
                            int32_t* split_indptr, hipStream_t stream);
 
+/*
+ * mla_build_table_and_plan — mla_build_block_table and mla_plan_splits in
+ * one launch (init_forward_metadata of both page backends computes the block
+ * table and the split metadata together, once per batch step).  One work-group
+ * plans while the others fill the table, so the step pays for one small
+ * launch instead of two.
+ *
+ * Arguments are those of the two calls (same meaning, same layouts), and the
+ * results are bit for bit theirs.  Errors: those of mla_build_block_table,
+ * then those of mla_plan_splits, checked before anything is launched;
+ * UNSUPPORTED if the table needs more than 2^31 - 2 work-groups.
+ */
+mla_status mla_build_table_and_plan(const int32_t* req_to_token, int32_t r2t_rows,
+                                    int64_t r2t_row_stride, const int32_t* req_pool_indices,
+                                    const int32_t* seq_lens, int32_t bs, int32_t page_size,
+                                    int32_t* block_table, int32_t bt_row_stride,
+                                    int32_t pad_value, int32_t max_seq_len_hint,
+                                    int32_t rows_per_req, int32_t num_parts, int32_t kv_dtype,
+                                    int32_t* tile_plan, int32_t* split_indptr,
+                                    hipStream_t stream);
+
 /* Host helpers: upper bound of split_indptr[bs] (= bs + num_parts), and the
  * bytes of the partial_o + partial_lse buffers that bound needs. */
 int32_t mla_max_total_splits(int32_t bs, int32_t num_parts);

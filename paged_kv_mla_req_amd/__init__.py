@@ -110,6 +110,41 @@ def plan_splits(seq_lens: torch.Tensor, rows_per_req: int, num_parts: Optional[i
     return tile_plan[:num_parts], split_indptr[:bs + 1]
 
 
+def build_table_and_plan(req_to_token: torch.Tensor, req_pool_indices: torch.Tensor,
+                         seq_lens: torch.Tensor, width: int, rows_per_req: int,
+                         num_parts: Optional[int] = None, kv_dtype="bf16", pad_value: int = -1,
+                         max_seq_len_hint: int = -1, out: Optional[torch.Tensor] = None,
+                         tile_plan: Optional[torch.Tensor] = None,
+                         split_indptr: Optional[torch.Tensor] = None, stream=None):
+    """(block_table, tile_plan, split_indptr) from one launch
+    (mla_build_table_and_plan): the results of build_block_table and
+    plan_splits."""
+    _need(req_to_token, "req_to_token", (torch.int32,), 2)
+    _need(req_pool_indices, "req_pool_indices", (torch.int32,), 1)
+    _need(seq_lens, "seq_lens", (torch.int32,), 1)
+    bs = seq_lens.shape[0]
+    dev = seq_lens.device
+    if num_parts is None:
+        num_parts = device_num_cus()
+    if out is None:
+        out = torch.empty((bs, width), dtype=torch.int32, device=dev)
+    if tile_plan is None:
+        tile_plan = torch.empty((num_parts, 8), dtype=torch.int32, device=dev)
+    if split_indptr is None:
+        split_indptr = torch.empty((bs + 1,), dtype=torch.int32, device=dev)
+    _need(out, "out", (torch.int32,), 2)
+    _need(tile_plan, "tile_plan", (torch.int32,), 2)
+    _need(split_indptr, "split_indptr", (torch.int32,), 1)
+    if tile_plan.shape[0] < num_parts or split_indptr.shape[0] < bs + 1:
+        raise ValueError("plan buffers too small")
+    _lib.check(_lib.lib().mla_build_table_and_plan(
+        _p(req_to_token), req_to_token.shape[0], req_to_token.stride(0), _p(req_pool_indices),
+        _p(seq_lens), bs, PAGE_SIZE, _p(out), out.shape[1], pad_value, max_seq_len_hint,
+        rows_per_req, num_parts, _kv_code(kv_dtype), _p(tile_plan), _p(split_indptr),
+        _stream(stream)))
+    return out, tile_plan[:num_parts], split_indptr[:bs + 1]
+
+
 def partial_buffers(bs: int, rows_per_req: int, num_parts: int,
                     device="cuda") -> Tuple[torch.Tensor, torch.Tensor]:
     """Workspace for split pieces: partial o fp32 [bs+num_parts, R, 512] and

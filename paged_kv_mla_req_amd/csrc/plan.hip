@@ -10,7 +10,7 @@
 // to the nearest page boundary after dropping the first c units of its
 // request.  One work-group does everything: prefix sums over requests,
 // binary searches for the rest.  Deterministic.
-#include "common.h"
+#include "block_table.h"
 
 namespace mla {
 
@@ -70,13 +70,18 @@ __device__ __forceinline__ int lower_bound(const int* a, int n, int x) {
   return lo;
 }
 
-// One work-group of 4 waves: each thread takes a contiguous chunk of the
-// requests (and of the cuts), prefix sums are block scans, lookups are
-// binary searches in LDS.
-__global__ void __launch_bounds__(kPlanThreads)
-plan_splits_kernel(const int32_t* __restrict__ seq_lens, int bs, int overhead, int parts,
-                   int32_t* __restrict__ tile_plan, int32_t* __restrict__ split_indptr) {
-  extern __shared__ int smem[];
+// LDS the planning work-group needs (ints).
+__host__ __device__ __forceinline__ size_t plan_lds_ints(int bs, int parts) {
+  return 2 * (size_t)(bs + 1) + (size_t)(parts + 1) + (size_t)(parts + 2) + kPlanWaves;
+}
+
+// The plan, computed by one work-group of 4 waves: each thread takes a
+// contiguous chunk of the requests (and of the cuts), prefix sums are block
+// scans, lookups are binary searches in LDS (smem: plan_lds_ints ints).
+__device__ __forceinline__ void plan_body(int* smem, const int32_t* __restrict__ seq_lens,
+                                          int bs, int overhead, int parts,
+                                          int32_t* __restrict__ tile_plan,
+                                          int32_t* __restrict__ split_indptr) {
   int* cum = smem;                    // [bs + 1] cost prefix (quarter pages)
   int* pagecum = cum + (bs + 1);      // [bs + 1] page prefix
   int* cuts = pagecum + (bs + 1);     // [parts + 1] flattened page of each cut
@@ -196,39 +201,119 @@ plan_splits_kernel(const int32_t* __restrict__ seq_lens, int bs, int overhead, i
   }
 }
 
+__global__ void __launch_bounds__(kPlanThreads)
+plan_splits_kernel(const int32_t* __restrict__ seq_lens, int bs, int overhead, int parts,
+                   int32_t* __restrict__ tile_plan, int32_t* __restrict__ split_indptr) {
+  extern __shared__ int smem[];
+  plan_body(smem, seq_lens, bs, overhead, parts, tile_plan, split_indptr);
+}
+
+// Block table and plan in one launch (init_forward_metadata computes both
+// for a batch step): work-group 0 plans, the others fill the table, 256 cells
+// of one request each, while the plan's dependent steps run.
+__global__ void __launch_bounds__(kPlanThreads)
+table_and_plan_kernel(const int32_t* __restrict__ req_to_token, int32_t r2t_rows,
+                      int64_t r2t_row_stride, const int32_t* __restrict__ req_pool_indices,
+                      const int32_t* __restrict__ seq_lens, int32_t* __restrict__ block_table,
+                      int32_t bt_row_stride, int32_t pad_value, int bt_blocks_per_row, int bs,
+                      int overhead, int parts, int32_t* __restrict__ tile_plan,
+                      int32_t* __restrict__ split_indptr) {
+  extern __shared__ int smem[];
+  if (blockIdx.x == 0) {
+    plan_body(smem, seq_lens, bs, overhead, parts, tile_plan, split_indptr);
+    return;
+  }
+  const int w = blockIdx.x - 1;
+  const int b = w / bt_blocks_per_row;
+  const int p = (w - b * bt_blocks_per_row) * kPlanThreads + threadIdx.x;
+  if (p < bt_row_stride)
+    block_table_cell(b, p, req_to_token, r2t_rows, r2t_row_stride, req_pool_indices, seq_lens,
+                     block_table, bt_row_stride, pad_value);
+}
+
+}  // namespace mla
+
+namespace mla {
+
+mla_status check_plan_args(const char* who, const int32_t* seq_lens, int32_t bs,
+                           int32_t rows_per_req, int32_t num_parts, int32_t kv_dtype,
+                           const int32_t* tile_plan, const int32_t* split_indptr) {
+  const std::string w(who);
+  if (!seq_lens || !tile_plan || !split_indptr)
+    return fail(MLA_ERR_INVALID_ARGUMENT, w + ": null pointer");
+  if (bs <= 0 || num_parts <= 0)
+    return fail(MLA_ERR_INVALID_ARGUMENT, w + ": bs and num_parts must be positive");
+  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3)
+    return fail(MLA_ERR_INVALID_ARGUMENT, w + ": unknown kv_dtype");
+  if (rows_per_req < 1 || rows_per_req > MLA_MAX_ROWS_PER_REQ)
+    return fail(MLA_ERR_UNSUPPORTED, w + ": rows_per_req must be in 1..512");
+  if (bs > MLA_MAX_BATCH)
+    return fail(MLA_ERR_CAPACITY, w + ": bs above " + std::to_string(MLA_MAX_BATCH));
+  if (num_parts > MLA_MAX_PARTS)
+    return fail(MLA_ERR_CAPACITY, w + ": num_parts above " + std::to_string(MLA_MAX_PARTS));
+  int cus = mla_device_num_cus();
+  if (cus > 0 && num_parts > cus)
+    return fail(MLA_ERR_CAPACITY, w + ": num_parts " + std::to_string(num_parts) +
+                                      " exceeds the device's " + std::to_string(cus) + " CUs");
+  return MLA_OK;
+}
+
+// Raises the dynamic-LDS limit of a planning kernel once.
+template <typename K>
+mla_status allow_plan_lds(K kernel, bool& done, const char* who) {
+  if (!done) {
+    if (hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            160 * 1024) != hipSuccess)
+      return fail(MLA_ERR_DEVICE, std::string(who) + ": cannot raise the LDS limit");
+    done = true;
+  }
+  return MLA_OK;
+}
+
 }  // namespace mla
 
 extern "C" mla_status mla_plan_splits(const int32_t* seq_lens, int32_t bs, int32_t rows_per_req,
                                       int32_t num_parts, int32_t kv_dtype, int32_t* tile_plan,
                                       int32_t* split_indptr, hipStream_t stream) {
   using namespace mla;
-  if (!seq_lens || !tile_plan || !split_indptr)
-    return fail(MLA_ERR_INVALID_ARGUMENT, "mla_plan_splits: null pointer");
-  if (bs <= 0 || num_parts <= 0)
-    return fail(MLA_ERR_INVALID_ARGUMENT, "mla_plan_splits: bs and num_parts must be positive");
-  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3)
-    return fail(MLA_ERR_INVALID_ARGUMENT, "mla_plan_splits: unknown kv_dtype");
-  if (rows_per_req < 1 || rows_per_req > MLA_MAX_ROWS_PER_REQ)
-    return fail(MLA_ERR_UNSUPPORTED, "mla_plan_splits: rows_per_req must be in 1..512");
-  if (bs > MLA_MAX_BATCH)
-    return fail(MLA_ERR_CAPACITY, "mla_plan_splits: bs above " + std::to_string(MLA_MAX_BATCH));
-  if (num_parts > MLA_MAX_PARTS)
-    return fail(MLA_ERR_CAPACITY, "mla_plan_splits: num_parts above " + std::to_string(MLA_MAX_PARTS));
-  int cus = mla_device_num_cus();
-  if (cus > 0 && num_parts > cus)
-    return fail(MLA_ERR_CAPACITY, "mla_plan_splits: num_parts " + std::to_string(num_parts) +
-                                      " exceeds the device's " + std::to_string(cus) + " CUs");
+  const mla_status st = check_plan_args("mla_plan_splits", seq_lens, bs, rows_per_req, num_parts,
+                                        kv_dtype, tile_plan, split_indptr);
+  if (st != MLA_OK) return st;
   const int overhead = plan_overhead_q(rows_per_req);
-  const size_t lds = sizeof(int) * (2 * (size_t)(bs + 1) + (size_t)(num_parts + 1) +
-                                    (size_t)(num_parts + 2) + kPlanWaves);
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)plan_splits_kernel,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
-      return fail(MLA_ERR_DEVICE, "mla_plan_splits: cannot raise the LDS limit");
-    attr_set = true;
-  }
+  const size_t lds = sizeof(int) * plan_lds_ints(bs, num_parts);
+  static bool lds_raised = false;
+  const mla_status la = allow_plan_lds(plan_splits_kernel, lds_raised, "mla_plan_splits");
+  if (la != MLA_OK) return la;
   hipLaunchKernelGGL(plan_splits_kernel, dim3(1), dim3(kPlanThreads), lds, stream, seq_lens, bs,
                      overhead, num_parts, tile_plan, split_indptr);
   return check_launch("mla_plan_splits");
+}
+
+extern "C" mla_status mla_build_table_and_plan(
+    const int32_t* req_to_token, int32_t r2t_rows, int64_t r2t_row_stride,
+    const int32_t* req_pool_indices, const int32_t* seq_lens, int32_t bs, int32_t page_size,
+    int32_t* block_table, int32_t bt_row_stride, int32_t pad_value, int32_t max_seq_len_hint,
+    int32_t rows_per_req, int32_t num_parts, int32_t kv_dtype, int32_t* tile_plan,
+    int32_t* split_indptr, hipStream_t stream) {
+  using namespace mla;
+  const char* who = "mla_build_table_and_plan";
+  mla_status st = check_block_table_args(who, req_to_token, r2t_rows, r2t_row_stride,
+                                         req_pool_indices, seq_lens, bs, page_size, block_table,
+                                         bt_row_stride, max_seq_len_hint);
+  if (st != MLA_OK) return st;
+  st = check_plan_args(who, seq_lens, bs, rows_per_req, num_parts, kv_dtype, tile_plan,
+                       split_indptr);
+  if (st != MLA_OK) return st;
+  const int per_row = (bt_row_stride + kPlanThreads - 1) / kPlanThreads;
+  const int64_t blocks = 1 + (int64_t)bs * per_row;
+  if (blocks > 0x7fffffff) return fail(MLA_ERR_UNSUPPORTED, std::string(who) + ": table too large");
+  const size_t lds = sizeof(int) * plan_lds_ints(bs, num_parts);
+  static bool lds_raised = false;
+  st = allow_plan_lds(table_and_plan_kernel, lds_raised, who);
+  if (st != MLA_OK) return st;
+  hipLaunchKernelGGL(table_and_plan_kernel, dim3((unsigned)blocks), dim3(kPlanThreads), lds,
+                     stream, req_to_token, r2t_rows, r2t_row_stride, req_pool_indices, seq_lens,
+                     block_table, bt_row_stride, pad_value, per_row, bs,
+                     plan_overhead_q(rows_per_req), num_parts, tile_plan, split_indptr);
+  return check_launch(who);
 }

@@ -100,3 +100,28 @@ def test_plan_and_merge_argument_errors():
     assert m(None, FAKE, FAKE, 2, 16, FAKE, None, None) == _lib.MLA_ERR_INVALID_ARGUMENT
     assert m(FAKE, FAKE, FAKE, 0, 16, FAKE, None, None) == _lib.MLA_ERR_INVALID_ARGUMENT
     assert m(FAKE, FAKE, FAKE, 2, 513, FAKE, None, None) == _lib.MLA_ERR_UNSUPPORTED
+
+
+def test_table_and_plan_argument_errors():
+    """The fused call checks both calls' arguments before any launch."""
+    f = _lib.lib().mla_build_table_and_plan
+    ok = dict(r2t=FAKE, rows=4, stride=256, rpi=FAKE, sl=FAKE, bs=2, page=64, bt=FAKE, bts=3,
+              pad=-1, hint=-1, rpr=16, parts=4, dtype=0, tp=FAKE, ip=FAKE)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["r2t"], a["rows"], a["stride"], a["rpi"], a["sl"], a["bs"], a["page"], a["bt"],
+                 a["bts"], a["pad"], a["hint"], a["rpr"], a["parts"], a["dtype"], a["tp"],
+                 a["ip"], None)
+
+    assert call(r2t=None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert call(bt=None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert call(tp=None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert call(bs=0) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert call(page=32) == _lib.MLA_ERR_UNSUPPORTED
+    assert call(hint=200) == _lib.MLA_ERR_CAPACITY          # needs 4 pages, table has 3
+    assert call(rpr=0) == _lib.MLA_ERR_UNSUPPORTED
+    assert call(parts=600) == _lib.MLA_ERR_CAPACITY
+    assert call(dtype=5) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert _lib.lib().mla_last_error_message().startswith(b"mla_build_table_and_plan")

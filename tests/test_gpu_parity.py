@@ -134,6 +134,28 @@ def test_plan_edge_shapes(mla, lens, parts, rows):
     assert np.array_equal(tp, rt) and np.array_equal(ip, rip)
 
 
+@pytest.mark.parametrize("name,parts", [("tiny", 3), ("dsv3", 256), ("long", 256),
+                                        ("verify", 256), ("fp8", 100)])
+def test_table_and_plan_in_one_launch(mla, name, parts):
+    """mla_build_table_and_plan gives the block table of mla_build_block_table
+    and the plan of mla_plan_splits, bit for bit, and both match the oracle."""
+    w = make_workload(name) if name == "tiny" else _lens_only(name)
+    d = to_device(w)
+    rows = CONFIGS[name]["heads"] * CONFIGS[name]["q_len"]
+    for width, pad in ((w.bt_width, -1), (w.bt_width + 300, 7)):
+        bt, tp, ip = mla.build_table_and_plan(d.req_to_token, d.req_pool_indices, d.seq_lens,
+                                              width, rows, parts, pad_value=pad)
+        bt2 = mla.build_block_table(d.req_to_token, d.req_pool_indices, d.seq_lens, width, pad)
+        tp2, ip2 = mla.plan_splits(d.seq_lens, rows, parts)
+        bt, tp, ip = _np(bt), _np(tp), _np(ip)
+        assert np.array_equal(bt, _np(bt2))
+        assert np.array_equal(tp, _np(tp2)) and np.array_equal(ip, _np(ip2))
+        assert np.array_equal(bt, oracle.block_table(w.req_to_token, w.req_pool_indices,
+                                                     w.seq_lens, width, pad))
+        rt, rip = oracle.plan_reference(w.seq_lens, parts, rows)
+        assert np.array_equal(tp, rt) and np.array_equal(ip, rip)
+
+
 def test_plan_rejects_more_parts_than_cus(mla):
     sl = torch.ones(4, dtype=torch.int32, device="cuda")
     with pytest.raises(mla.MLAError):
