@@ -31,9 +31,9 @@ COMMON_FLAGS = [
 ]
 
 # The decode kernel is compiled without NaN semantics, so that max() over
-# scores is a plain v_max/v_max3 (no operand canonicalisation).  Only finite
-# scores reach it: page tails are zero-filled and masked keys are selected
-# out, never multiplied.
+# scores is a plain v_max/v_max3 (no operand canonicalisation).  No NaN
+# reaches it from the cache's unused slots: page tails are zero-filled, and
+# masked scores are -inf, scaled by a factor kept above 0.
 SOURCE_FLAGS = {"decode.hip": ["-fno-honor-nans"]}
 
 
