@@ -782,15 +782,29 @@ __device__ __forceinline__ void store_rows(const f32x16 (&oacc)[kVTiles], float 
     ra[qq] = reinterpret_cast<const uint4*>(stage + row * 128 + ((j ^ (row & 7)) << 4));
     rowp[qq] = dst + (int64_t)(row0 + row) * kDv + 4 * j;
   }
+  // Tile p + 1 goes to LDS and is read back while tile p is scaled and
+  // stored: a wave's LDS operations run in order, so the writes of tile p + 1
+  // land after the reads of tile p have taken the old contents.
+  auto stage_tile = [&](const f32x16& tile) {
+    stage_quad<0>(tile, wa[0]);
+    stage_quad<1>(tile, wa[1]);
+    stage_quad<2>(tile, wa[2]);
+    stage_quad<3>(tile, wa[3]);
+  };
+  uint4 cur[4], nxt[4];
+  stage_tile(oacc[0]);
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) cur[qq] = *ra[qq];
 #pragma unroll
   for (int p = 0; p < kVTiles; ++p) {
-    stage_quad<0>(oacc[p], wa[0]);
-    stage_quad<1>(oacc[p], wa[1]);
-    stage_quad<2>(oacc[p], wa[2]);
-    stage_quad<3>(oacc[p], wa[3]);
+    if (p + 1 < kVTiles) {
+      stage_tile(oacc[p + 1]);
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) nxt[qq] = *ra[qq];
+    }
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
-      const float4 v = __builtin_bit_cast(float4, *ra[qq]);
+      const float4 v = __builtin_bit_cast(float4, cur[qq]);
       const float x0 = v.x * rs[qq], x1 = v.y * rs[qq], x2 = v.z * rs[qq], x3 = v.w * rs[qq];
       if (FULL || row0 + 8 * qq + (int)(lane >> 3) < rows) {
         if constexpr (kBf16) {
@@ -804,7 +818,9 @@ __device__ __forceinline__ void store_rows(const f32x16 (&oacc)[kVTiles], float 
         }
       }
     }
-    __builtin_amdgcn_sched_barrier(0);  // one tile of registers live at a time
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) cur[qq] = nxt[qq];
+    __builtin_amdgcn_sched_barrier(0);  // two tiles of registers live at a time
   }
 }
 
