@@ -8,8 +8,9 @@
 // costs 4 N_b + c (c: the per-piece overhead of plan_overhead_q), part p
 // covers cost positions [floor(pC/P), floor((p+1)C/P)), and a position maps
 // to the nearest page boundary after dropping the first c units of its
-// request.  One work-group does everything: prefix sums over requests,
-// binary searches for the rest.  Deterministic.
+// request.  One work-group does everything: prefix sums over requests, a
+// binary search per cut for its cost position, and per-cut bookkeeping for the
+// rest.  Deterministic.
 #include "block_table.h"
 
 namespace mla {
@@ -72,21 +73,30 @@ __device__ __forceinline__ int lower_bound(const int* a, int n, int x) {
 
 // LDS the planning work-group needs (ints).
 __host__ __device__ __forceinline__ size_t plan_lds_ints(int bs, int parts) {
-  return 2 * (size_t)(bs + 1) + (size_t)(parts + 1) + (size_t)(parts + 2) + kPlanWaves;
+  return 2 * (size_t)(bs + 1) + 3 * (size_t)(parts + 1) + (size_t)(parts + 2) + kPlanWaves;
 }
 
 // The plan, computed by one work-group of 4 waves: each thread takes a
-// contiguous chunk of the requests (and of the cuts), prefix sums are block
-// scans, lookups are binary searches in LDS (smem: plan_lds_ints ints).
+// contiguous chunk of the requests (and of the cuts) and prefix sums are
+// block scans.  Each cut carries the request its cost position falls in and
+// its page offset there, so the per-request piece counts and the table rows
+// need no searches except where a cut sits on a request boundary.
+// smem: plan_lds_ints ints.
 __device__ __forceinline__ void plan_body(int* smem, const int32_t* __restrict__ seq_lens,
                                           int bs, int overhead, int parts,
                                           int32_t* __restrict__ tile_plan,
                                           int32_t* __restrict__ split_indptr) {
-  int* cum = smem;                    // [bs + 1] cost prefix (quarter pages)
-  int* pagecum = cum + (bs + 1);      // [bs + 1] page prefix
-  int* cuts = pagecum + (bs + 1);     // [parts + 1] flattened page of each cut
-  int* fcum = cuts + (parts + 1);     // [parts + 2] prefix count of distinct interior cuts
-  int* wave_tot = fcum + (parts + 2); // [kPlanWaves]
+  // cum is dead after step 2: its space then counts each request's interior
+  // cuts (extra), and after step 4 holds ubr.
+  int* cum = smem;                     // [bs + 1] cost prefix (quarter pages)
+  int* extra = cum;                    // [bs + 1] distinct interior cuts per request
+  int* ubr = cum;                      // [bs + 1] first cut index beyond a request's start
+  int* pagecum = cum + (bs + 1);       // [bs + 1] page prefix
+  int* cuts = pagecum + (bs + 1);      // [parts + 1] flattened page of each cut
+  int* cut_b = cuts + (parts + 1);     // [parts + 1] request of the cut's cost position
+  int* cut_k = cut_b + (parts + 1);    // [parts + 1] cut page offset inside that request
+  int* fcum = cut_k + (parts + 1);     // [parts + 2] prefix count of distinct interior cuts
+  int* wave_tot = fcum + (parts + 2);  // [kPlanWaves]
 
   const int t = threadIdx.x;
   const int chunk = (bs + kPlanThreads - 1) / kPlanThreads;
@@ -121,36 +131,42 @@ __device__ __forceinline__ void plan_body(int* smem, const int32_t* __restrict__
   // 2. cut positions -> flattened page boundaries (nearest page boundary,
   //    the first `overhead` units of a request mapping to its page 0)
   for (int p = t; p <= parts; p += kPlanThreads) {
-    int g;
+    int g, b = bs, k = 0;
     const int64_t x = (int64_t)p * C / parts;
     if (p == parts || x >= C) {
       g = total_pages;
     } else {
-      const int b = upper_bound(cum, bs, (int)x) - 1;
+      b = upper_bound(cum, bs, (int)x) - 1;
       const int o = (int)x - cum[b];
       const int n = pagecum[b + 1] - pagecum[b];
-      g = pagecum[b] + min(max(o - overhead + 2, 0) >> 2, n);
+      k = min(max(o - overhead + 2, 0) >> 2, n);
+      g = pagecum[b] + k;
     }
     cuts[p] = g;
+    cut_b[p] = b;
+    cut_k[p] = k;
   }
   __syncthreads();
+  for (int b = b_begin; b < b_end; ++b) extra[b] = 0;
+  __syncthreads();
 
-  // 3. distinct interior cuts (strictly inside a request), prefix-counted
+  // 3. distinct interior cuts (strictly inside a request), prefix-counted, and
+  //    counted per request
   const int pchunk = (parts + 1 + kPlanThreads - 1) / kPlanThreads;
   const int p_begin = min(parts + 1, t * pchunk);
   const int p_end = min(parts + 1, p_begin + pchunk);
   auto interior = [&](int p) -> int {
     if (p < 1 || p >= parts) return 0;
-    const int g = cuts[p];
-    if (g <= 0 || g >= total_pages || g == cuts[p - 1]) return 0;
-    const int b = upper_bound(pagecum, bs, g) - 1;
-    return (g - pagecum[b]) > 0;
+    const int b = cut_b[p], k = cut_k[p];
+    if (b >= bs || k <= 0 || k >= pagecum[b + 1] - pagecum[b]) return 0;
+    return cuts[p] != cuts[p - 1];
   };
   int flags[4] = {0, 0, 0, 0};  // pchunk <= 3 for parts <= 512
   int my_flags = 0;
   for (int p = p_begin; p < p_end; ++p) {
     const int f = interior(p);
     if (p - p_begin < 4) flags[p - p_begin] = f;
+    if (f) atomicAdd(&extra[cut_b[p]], 1);
     my_flags += f;
   }
   int n_interior;
@@ -163,36 +179,42 @@ __device__ __forceinline__ void plan_body(int* smem, const int32_t* __restrict__
   __syncthreads();
 
   // 4. pieces per request -> split_indptr
-  auto pieces_of = [&](int b) -> int {
-    const int lo = pagecum[b], hi = pagecum[b + 1];
-    if (hi == lo) return 0;
-    const int i_lo = upper_bound(cuts, parts + 1, lo);
-    const int i_hi = lower_bound(cuts, parts + 1, hi);
-    return 1 + (i_hi > i_lo ? fcum[i_hi] - fcum[i_lo] : 0);
-  };
   int my_pieces = 0;
-  for (int b = b_begin; b < b_end; ++b) my_pieces += pieces_of(b);
+  for (int b = b_begin; b < b_end; ++b) {
+    const int np = pagecum[b + 1] > pagecum[b] ? 1 + extra[b] : 0;
+    extra[b] = np;  // now the request's piece count
+    my_pieces += np;
+  }
   int n_pieces;
   int piece_off = block_exclusive_scan(my_pieces, wave_tot, &n_pieces);
   for (int b = b_begin; b < b_end; ++b) {
     split_indptr[b] = piece_off;
-    piece_off += pieces_of(b);
+    piece_off += extra[b];
   }
   if (t == 0) split_indptr[bs] = n_pieces;
+  __syncthreads();
+  for (int b = b_begin; b < b_end; ++b) ubr[b] = upper_bound(cuts, parts + 1, pagecum[b]);
+  __syncthreads();
 
   // 5. one table row per part
   for (int p = t; p < parts; p += kPlanThreads) {
     int row[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     const int g0 = cuts[p], g1 = cuts[p + 1];
     if (g1 > g0) {
-      const int b0 = upper_bound(pagecum, bs, g0) - 1;
-      const int b1 = upper_bound(pagecum, bs, g1 - 1) - 1;
+      // request of page g0: the cut's own request unless the cut ends it
+      const int cb0 = cut_b[p];
+      const int b0 = (cb0 < bs && cut_k[p] < pagecum[cb0 + 1] - pagecum[cb0])
+                         ? cb0
+                         : upper_bound(pagecum, bs, g0) - 1;
+      // request of page g1 - 1: the next cut's request unless that cut starts it
+      const int b1 = (cut_b[p + 1] < bs && cut_k[p + 1] > 0)
+                         ? cut_b[p + 1]
+                         : upper_bound(pagecum, bs, g1 - 1) - 1;
       row[0] = b0;
       row[1] = g0 - pagecum[b0];
       row[2] = b1;
       row[3] = g1 - pagecum[b1];
-      row[4] = fcum[upper_bound(cuts, parts + 1, g0)] -
-               fcum[upper_bound(cuts, parts + 1, pagecum[b0])];
+      row[4] = fcum[p + 1] - fcum[ubr[b0]];
       row[5] = g1 - g0;
     }
     int4* dst = reinterpret_cast<int4*>(tile_plan + p * 8);
