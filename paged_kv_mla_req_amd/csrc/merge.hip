@@ -7,16 +7,17 @@
 // does the k-way form for every request whose keys mla_decode split into k
 // pieces:  LSE = M + ln sum_k exp(lse_k - M),  o = sum_k exp(lse_k - LSE) o_k.
 //
-// One wave per (request, row): the lanes first take one piece's lse each
-// (wave max and sum), then each lane owns 8 of the 512 value columns (two
-// 16-byte loads per piece, so a piece's row is read fully coalesced), with
-// the rows of four pieces in flight at a time.  Pure HBM streaming; no MFMA.
+// One wave per (request, row): each lane owns 8 of the 512 value columns (two
+// 16-byte loads per piece, so a piece's row is read fully coalesced), with the
+// rows of eight pieces in flight at a time; for up to 64 pieces the lanes take
+// one piece's lse each (wave max and sum) while the first rows are already
+// loading, so a row costs one memory round trip.  Pure HBM streaming; no MFMA.
 #include "common.h"
 
 namespace mla {
 
 constexpr int kMergeWaves = 4;
-constexpr int kMergeBatch = 4;  // pieces whose rows are loaded together
+constexpr int kMergeBatch = 8;  // pieces whose rows are loaded together
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -44,7 +45,51 @@ merge_states_kernel(const float* __restrict__ partial_o, const float* __restrict
 
   float4 acc0 = make_float4(0.f, 0.f, 0.f, 0.f), acc1 = acc0;
   float LSE = -INFINITY;
-  if (k > 1) {
+  if (k > 1 && k <= 64) {
+    // One round trip: lane s takes piece s's lse while the rows of the first
+    // kMergeBatch pieces are already on their way (they do not depend on it).
+    const float l = lane < k ? partial_lse[(int64_t)(k0 + lane) * rows + r] : -INFINITY;
+    float4 x0[kMergeBatch], x1[kMergeBatch];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      x0[j] = x1[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j < k) {
+        const float4* src =
+            reinterpret_cast<const float4*>(partial_o + ((int64_t)(k0 + j) * rows + r) * kDv) +
+            lane * 2;
+        x0[j] = src[0];
+        x1[j] = src[1];
+      }
+    }
+    const float M = wave_max(l);
+    if (M != -INFINITY) {
+      LSE = M + __logf(wave_sum(l == -INFINITY ? 0.f : __expf(l - M)));
+      const float wl = l == -INFINITY ? 0.f : __expf(l - LSE);  // piece `lane`'s weight
+      for (int s0 = 0; s0 < k; s0 += kMergeBatch) {
+        if (s0 > 0) {
+#pragma unroll
+          for (int j = 0; j < kMergeBatch; ++j) {
+            x0[j] = x1[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (s0 + j < k) {
+              const float4* src = reinterpret_cast<const float4*>(
+                                      partial_o + ((int64_t)(k0 + s0 + j) * rows + r) * kDv) +
+                                  lane * 2;
+              x0[j] = src[0];
+              x1[j] = src[1];
+            }
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) {
+          const float w = __shfl(wl, (s0 + j) & 63, 64);  // 0 past the last piece
+          acc0.x += w * x0[j].x; acc0.y += w * x0[j].y;
+          acc0.z += w * x0[j].z; acc0.w += w * x0[j].w;
+          acc1.x += w * x1[j].x; acc1.y += w * x1[j].y;
+          acc1.z += w * x1[j].z; acc1.w += w * x1[j].w;
+        }
+      }
+    }
+  } else if (k > 64) {
     // M and the sum of exp(lse - M): the lanes take the pieces' lse values
     float m = -INFINITY;
     for (int s = lane; s < k; s += 64) m = fmaxf(m, partial_lse[(int64_t)(k0 + s) * rows + r]);
