@@ -81,6 +81,17 @@ constexpr int kLoadsPerWave = kLoadsPerPage / kWaves;    // 18
 constexpr int kKSteps = kD / 16;                         // 36 MFMA k-steps for S
 constexpr int kVTiles = kDv / 32;                        // 16 output tiles of 32 columns
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
+constexpr int kXcds = 8;      // accelerator dies, each with its own L2
+
+// Work-groups go to the dies round robin (work-group i to die i % 8).
+// Neighbouring parts mostly hold pieces of the same request, which load the
+// same query rows: part_of_block gives each die a contiguous run of parts, so
+// those loads hit the die's L2 after the first.  A bijection of [0, parts).
+__device__ __forceinline__ int part_of_block(int i, int parts) {
+  const int x = i % kXcds, j = i / kXcds;
+  const int per = parts / kXcds, extra = parts % kXcds;
+  return x * per + min(x, extra) + j;
+}
 // The page loop issues the next page's loads one per block of four MFMAs of
 // the first score tile (e4m3: all 9; bf16: 9 of 18), the rest of bf16 one
 // every third slot early in the second tile's chain.
@@ -841,7 +852,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int lane = (int)lane_id();  // used before the page loops only
-  const int part = blockIdx.x;
+  const int part = part_of_block(blockIdx.x, gridDim.x);
 
   const int32_t* tp = tile_plan + part * 8;
   const int b_first = tp[0], pg_first = tp[1], b_last = tp[2], pg_last = tp[3];
