@@ -940,6 +940,18 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
     return;
   }
 
+  // Range of the cursor's page for the loads issued during the page before
+  // it.  It is worked out (and the cursor moved on, which starts the read of
+  // the block-table entry after it) one page ahead, among the last output
+  // MFMAs of a page, where the wave has issue slots to spare.
+  __amdgpu_buffer_rsrc_t next_rsrc;
+  auto next_range = [&](bool has) {
+    next_rsrc = page_rsrc<FP8 ? kD : kRowBytes>(
+        kv + nphys() * kSrcPageBytes, has ? __builtin_amdgcn_readfirstlane(nrows) : 0);
+  };
+  next_range(1 < total);
+  if (1 < total) advance();
+
   // Per-tensor dequantisation scale: scores use |delta| in the softmax scale
   // and the sign on q; the output is multiplied by delta.
   const float delta = FP8 ? kv_descale[0] : 1.0f;
@@ -1018,20 +1030,12 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
       const lds_u8* base = LDS_PTR(uint8_t, smem) + (FP8 ? 0 : (it & 1) * kPageBytes);
       // The next page's loads are spread over the MFMA work (issued back to
       // back they would stall the wave until the address unit drains them).
-      // Their range and the cursor's step to page it + 2 (whose block-table
-      // entry then has this whole page to arrive) are worked out in the shadow
-      // of the first MFMAs.  After the part's last page the loads still go out, over an
-      // empty range: they only write zeros into the free buffer (and cost no
-      // branch per load); the kernel waits for them before it ends.
-      const bool has_next = it + 1 < total;
-      __amdgpu_buffer_rsrc_t next_rsrc;
+      // Their range (next_rsrc) was worked out on the previous page.  After the
+      // part's last page the loads still go out, over an empty range: they
+      // only write zeros into the free buffer (and cost no branch per load);
+      // the kernel waits for them before it ends.
       uint8_t* const next_buf = FP8 ? smem + kPageBytes + ((it + 1) & 1) * kPageBytesF8
                                     : smem + ((it + 1) & 1) * kPageBytes;
-      auto start_next = [&]() {
-        next_rsrc = page_rsrc<FP8 ? kD : kRowBytes>(
-            kv + nphys() * kSrcPageBytes, has_next ? __builtin_amdgcn_readfirstlane(nrows) : 0);
-        if (has_next) advance();
-      };
       // load K of this wave's share, K < 18 (bf16) or K < 9 (e4m3)
       auto load = [&](auto kc) {
         constexpr int K = decltype(kc)::value;
@@ -1040,11 +1044,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
         else
           issue_one_load<K>(next_rsrc, next_buf, wave, lo.load, lo.load + 4 * (8 * kRowBytes));
       };
-      auto hook_s0 = [&](auto g) {
-        constexpr int G = decltype(g)::value;
-        if constexpr (G == 0) start_next();
-        load(ic<G>{});
-      };
+      auto hook_s0 = [&](auto g) { load(g); };
       auto no_hook = [](auto) {};
       if constexpr (FP8) {
         convert_f8_page(smem + kPageBytes + (it & 1) * kPageBytesF8, smem, wave);
@@ -1204,6 +1204,10 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
               pop[1] = __builtin_bit_cast(bf16x8, (u32x4){pk[4], pk[5], pk[6], pk[7]});
           } else if constexpr (k == 13) {
             fold_ls();
+          } else if constexpr (k == 17) {
+            next_range(it + 2 < total);  // page it + 2, loaded during page it + 1
+          } else if constexpr (k == 21) {
+            if (it + 2 < total) advance();
           }
         };
         pv_tile<1>(oacc, pop, va, no_hook, pay_pv1);
