@@ -223,11 +223,175 @@ __device__ __forceinline__ void plan_body(int* smem, const int32_t* __restrict__
   }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: shifts inside rows of 16
+// lanes, then the last lane of row 0 (and 2) added to row 1 (and 3), then the
+// last lane of row 1 added to rows 2 and 3 (DPP; no LDS round trips).
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
+// Exclusive prefix sums of N ints per thread over the work-group, with one
+// barrier: wave sums go through wt (kPlanWaves * N ints of LDS, not reused
+// before the next barrier).  tot[i] gets the work-group total of value i.
+template <int N>
+__device__ __forceinline__ void block_exclusive_sums(int (&v)[N], int* wt, int (&tot)[N]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    inc[i] = wave_inclusive_sum(v[i]);
+    if (lane == 63) wt[wave * N + i] = inc[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kPlanWaves; ++w) {
+      const int t = wt[w * N + i];
+      before += w < wave ? t : 0;
+      all += t;
+    }
+    tot[i] = all;
+    v[i] = before + inc[i] - v[i];
+  }
+}
+
+// Exact floor / ceil of a * b / c for 0 <= a * b < 2^53 and c > 0: the quotient
+// is rounded once, and a non-integer quotient is at least 1/c from the next
+// integer, far more than the rounding error.
+__device__ __forceinline__ int floor_mul_div(int a, int b, int c) {
+  return (int)floor((double)a * (double)b / (double)c);
+}
+__device__ __forceinline__ int ceil_mul_div(int a, int b, int c) {
+  return (int)ceil((double)a * (double)b / (double)c);
+}
+
+// LDS the small-batch planner needs (ints).
+__host__ __device__ __forceinline__ size_t plan_small_lds_ints() {
+  return 8 * (size_t)(kPlanThreads + 1) + 4 * kPlanWaves;
+}
+
+// The same plan as plan_body for bs <= 256 and parts <= 256 (one thread per
+// request and one per part), with three barriers: each request finds the
+// parts whose cost position falls inside it by division (the part range is
+// [ceil(cum_b P / C), ceil(cum_{b+1} P / C))), places their cuts, counts its
+// distinct interior cuts (cuts are non-decreasing) and numbers its pieces;
+// the nonempty requests are listed in order, so the request before or after a
+// cut that sits on a request boundary is one lookup away.
+__device__ __forceinline__ void plan_small(int* smem, const int32_t* __restrict__ seq_lens,
+                                           int bs, int overhead, int parts,
+                                           int32_t* __restrict__ tile_plan,
+                                           int32_t* __restrict__ split_indptr) {
+  int* cum = smem;                               // [bs + 1] cost prefix (quarter pages)
+  int* pagecum = cum + (kPlanThreads + 1);       // [bs + 1] page prefix
+  int* rank = pagecum + (kPlanThreads + 1);      // [bs] index among nonempty requests
+  int* ne = rank + (kPlanThreads + 1);           // [nonempty] nonempty requests in order
+  int* cuts = ne + (kPlanThreads + 1);           // [parts + 1] flattened page of each cut
+  int* cut_b = cuts + (kPlanThreads + 1);        // [parts + 1] request of the cut
+  int* cut_k = cut_b + (kPlanThreads + 1);       // [parts + 1] page offset there
+  int* first = cut_k + (kPlanThreads + 1);       // [parts] first piece index of the part
+  int* wt = first + (kPlanThreads + 1);          // wave sums, 3 + 1 ints per wave
+
+  const int t = threadIdx.x;
+  const int L = t < bs ? seq_lens[t] : 0;
+  const int n = L > 0 ? (L + kPage - 1) / kPage : 0;
+  const int cost = n > 0 ? 4 * n + overhead : 0;
+  int v[3] = {cost, n, n > 0 ? 1 : 0}, tot[3];
+  block_exclusive_sums<3>(v, wt, tot);
+  const int C = tot[0], total_pages = tot[1], n_ne = tot[2];
+  if (t < bs) {
+    cum[t] = v[0];
+    pagecum[t] = v[1];
+    rank[t] = v[2];
+    if (n > 0) ne[v[2]] = t;
+  }
+  if (t == 0) {
+    cum[bs] = C;
+    pagecum[bs] = total_pages;
+  }
+  // every cut at the end, for a batch without pages (C = 0); otherwise each
+  // cut p < parts is placed below by the request its cost position falls in
+  if (t <= parts) cuts[t] = total_pages;
+  if (t == 0 && parts == kPlanThreads) cuts[parts] = total_pages;
+  __syncthreads();
+
+  // the cuts inside request t, its distinct interior cuts and piece numbers
+  int pieces = 0;
+  if (t < bs && n > 0) {
+    const int p_lo = ceil_mul_div(v[0], parts, C);
+    const int p_hi = min(parts, ceil_mul_div(v[0] + cost, parts, C));
+    int prev = -1, count = 0;
+    for (int p = p_lo; p < p_hi; ++p) {
+      const int o = floor_mul_div(p, C, parts) - v[0];
+      const int k = min(max(o - overhead + 2, 0) >> 2, n);
+      const int g = v[1] + k;
+      const bool inner = p > 0 && k > 0 && k < n;
+      if (inner && g != prev) ++count;
+      cuts[p] = g;
+      cut_b[p] = t;
+      cut_k[p] = k;
+      first[p] = inner ? count : 0;
+      prev = g;
+    }
+    pieces = 1 + count;
+  }
+  int pv[1] = {pieces}, ptot[1];
+  block_exclusive_sums<1>(pv, wt + 3 * kPlanWaves, ptot);  // also publishes the cuts
+  if (t < bs) split_indptr[t] = pv[0];
+  if (t == 0) split_indptr[bs] = ptot[0];
+
+  // one table row per part
+  if (t < parts) {
+    int row[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    const int g0 = cuts[t], g1 = cuts[t + 1];
+    if (g1 > g0) {
+      // request of page g0: the cut's own, or the next nonempty one if the cut ends it
+      const int cb0 = cut_b[t];
+      const int b0 = cut_k[t] < pagecum[cb0 + 1] - pagecum[cb0] ? cb0 : ne[rank[cb0] + 1];
+      // request of page g1 - 1: the next cut's own, or the nonempty one before
+      // it if that cut starts its request (or the last one for the final cut)
+      int b1;
+      if (t + 1 == parts) {
+        b1 = ne[n_ne - 1];
+      } else {
+        const int cb1 = cut_b[t + 1];
+        b1 = cut_k[t + 1] > 0 ? cb1 : ne[rank[cb1] - 1];
+      }
+      row[0] = b0;
+      row[1] = g0 - pagecum[b0];
+      row[2] = b1;
+      row[3] = g1 - pagecum[b1];
+      row[4] = first[t];
+      row[5] = g1 - g0;
+    }
+    int4* dst = reinterpret_cast<int4*>(tile_plan + t * 8);
+    dst[0] = make_int4(row[0], row[1], row[2], row[3]);
+    dst[1] = make_int4(row[4], row[5], row[6], row[7]);
+  }
+}
+
+// The planning work-group: the small-batch form when it applies.
+__device__ __forceinline__ void plan(int* smem, const int32_t* __restrict__ seq_lens, int bs,
+                                     int overhead, int parts, int32_t* __restrict__ tile_plan,
+                                     int32_t* __restrict__ split_indptr) {
+  if (bs <= kPlanThreads && parts <= kPlanThreads)
+    plan_small(smem, seq_lens, bs, overhead, parts, tile_plan, split_indptr);
+  else
+    plan_body(smem, seq_lens, bs, overhead, parts, tile_plan, split_indptr);
+}
+
 __global__ void __launch_bounds__(kPlanThreads)
 plan_splits_kernel(const int32_t* __restrict__ seq_lens, int bs, int overhead, int parts,
                    int32_t* __restrict__ tile_plan, int32_t* __restrict__ split_indptr) {
   extern __shared__ int smem[];
-  plan_body(smem, seq_lens, bs, overhead, parts, tile_plan, split_indptr);
+  plan(smem, seq_lens, bs, overhead, parts, tile_plan, split_indptr);
 }
 
 // Block table and plan in one launch (init_forward_metadata computes both
@@ -242,7 +406,7 @@ table_and_plan_kernel(const int32_t* __restrict__ req_to_token, int32_t r2t_rows
                       int32_t* __restrict__ split_indptr) {
   extern __shared__ int smem[];
   if (blockIdx.x == 0) {
-    plan_body(smem, seq_lens, bs, overhead, parts, tile_plan, split_indptr);
+    plan(smem, seq_lens, bs, overhead, parts, tile_plan, split_indptr);
     return;
   }
   const int w = blockIdx.x - 1;
@@ -280,6 +444,12 @@ mla_status check_plan_args(const char* who, const int32_t* seq_lens, int32_t bs,
   return MLA_OK;
 }
 
+// LDS ints of the planning work-group for a batch.
+inline size_t plan_lds(int bs, int parts) {
+  return (bs <= kPlanThreads && parts <= kPlanThreads) ? plan_small_lds_ints()
+                                                       : plan_lds_ints(bs, parts);
+}
+
 // Raises the dynamic-LDS limit of a planning kernel once.
 template <typename K>
 mla_status allow_plan_lds(K kernel, bool& done, const char* who) {
@@ -302,7 +472,7 @@ extern "C" mla_status mla_plan_splits(const int32_t* seq_lens, int32_t bs, int32
                                         kv_dtype, tile_plan, split_indptr);
   if (st != MLA_OK) return st;
   const int overhead = plan_overhead_q(rows_per_req);
-  const size_t lds = sizeof(int) * plan_lds_ints(bs, num_parts);
+  const size_t lds = sizeof(int) * plan_lds(bs, num_parts);
   static bool lds_raised = false;
   const mla_status la = allow_plan_lds(plan_splits_kernel, lds_raised, "mla_plan_splits");
   if (la != MLA_OK) return la;
@@ -329,7 +499,7 @@ extern "C" mla_status mla_build_table_and_plan(
   const int per_row = (bt_row_stride + kPlanThreads - 1) / kPlanThreads;
   const int64_t blocks = 1 + (int64_t)bs * per_row;
   if (blocks > 0x7fffffff) return fail(MLA_ERR_UNSUPPORTED, std::string(who) + ": table too large");
-  const size_t lds = sizeof(int) * plan_lds_ints(bs, num_parts);
+  const size_t lds = sizeof(int) * plan_lds(bs, num_parts);
   static bool lds_raised = false;
   st = allow_plan_lds(table_and_plan_kernel, lds_raised, who);
   if (st != MLA_OK) return st;

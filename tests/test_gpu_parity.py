@@ -124,6 +124,11 @@ def test_plan_matches_reference(mla, name, parts):
     ([1], 1, 16), ([1], 256, 16), ([64] * 300, 256, 128), ([65, 1, 64, 2000], 3, 64),
     ([0, 5, 0, 700], 4, 16), ([8192], 256, 512), ([129, 129, 129], 200, 128),
     (list(range(1, 2049)), 256, 128),
+    # one work-group per request and per part (bs, parts <= 256): empty requests
+    # first, last and in runs, cuts on request boundaries, more parts than pages
+    ([0] * 10 + [5000] + [0] * 245, 256, 128), ([0, 0, 64, 0], 256, 16), ([1] * 256, 255, 64),
+    ([64] * 256, 256, 128), ([0] * 256, 256, 16), ([0] * 255 + [1], 1, 16),
+    ([4096] * 64, 256, 128), ([64, 0, 0, 128, 0, 65], 5, 512), ([100000, 1], 256, 128),
 ])
 def test_plan_edge_shapes(mla, lens, parts, rows):
     lens = np.asarray(lens, dtype=np.int32)
