@@ -332,6 +332,17 @@ __device__ __forceinline__ void mfma_o(f32x16& o, const bf16x8& v, const bf16x8&
 
 __device__ __forceinline__ void mfma_tail() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
 
+// Clears the output accumulators with one MFMA per tile (zero operands, zero
+// accumulator input): 16 instructions instead of 256 register writes.  The
+// first one waits out the VALU write of the zero operand.
+__device__ __forceinline__ void zero_acc(f32x16 (&oacc)[kVTiles]) {
+  const bf16x8 z = {};
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(oacc[0]) : "v"(z));
+#pragma unroll
+  for (int vt = 1; vt < kVTiles; ++vt)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(oacc[vt]) : "v"(z));
+}
+
 // S^T chain: one 16-byte K-operand read per MFMA, from a ring of kKRing
 // operand slots.  The read for k-step ks+kKAhead is issued right after
 // MFMA ks, into the slot MFMA ks-1 used (its operands were read when it
@@ -470,6 +481,21 @@ __device__ __forceinline__ void v_reads(VSet& s, const uint32_t (&va)[2][2]) {
         [o0] "i"(PvOff<T, NB>::off0), [o1] "i"(PvOff<T, NB>::off1));
 }
 
+// Half H of v_reads (operands 2H and 2H + 1 of the set).
+template <int T, int NB, int H>
+__device__ __forceinline__ void v_reads_half(VSet& s, const uint32_t (&va)[2][2]) {
+  constexpr int o = H == 0 ? PvOff<T, NB>::off0 : PvOff<T, NB>::off1;
+  asm volatile(
+      "ds_read_b64_tr_b16 %[l0], %[a00] offset:%[o]\n\t"
+      "ds_read_b64_tr_b16 %[h0], %[a10] offset:%[o]\n\t"
+      "ds_read_b64_tr_b16 %[l1], %[a01] offset:%[o]\n\t"
+      "ds_read_b64_tr_b16 %[h1], %[a11] offset:%[o]"
+      : [l0] "=&v"(s.lo[2 * H]), [l1] "=&v"(s.lo[2 * H + 1]), [h0] "=&v"(s.hi[2 * H]),
+        [h1] "=&v"(s.hi[2 * H + 1])
+      : [a00] "v"(va[0][0]), [a10] "v"(va[1][0]), [a01] "v"(va[0][1]), [a11] "v"(va[1][1]),
+        [o] "i"(o));
+}
+
 // Wait until at most N LDS reads are outstanding; s becomes usable after it.
 template <int N>
 __device__ __forceinline__ void v_wait(VSet&) {
@@ -488,15 +514,23 @@ __device__ __forceinline__ void pv_mfma(f32x16 (&oacc)[kVTiles], const VSet& s,
   MLA_SB();
 }
 
+// The reads for group B + kAhead go out in two halves, before MFMAs 0 and 3
+// of the group, so that no gap between two MFMAs holds more than a few
+// instructions (the payload of slot 4B + 1 sits between MFMAs 1 and 2).
 template <int T, int B, typename Hook, typename Pay, int... J>
 __device__ __forceinline__ void pv_group(f32x16 (&oacc)[kVTiles], VSet (&ring)[kPvRing],
                                          const bf16x8 (&pop)[2], const uint32_t (&va)[2][2],
                                          Hook& hook, Pay& pay, std::integer_sequence<int, J...>) {
   constexpr int kAhead = kPvRing - 1;
-  if constexpr (B + kAhead < kPvBlocks)
-    v_reads<T, B + kAhead>(ring[(B + kAhead) % kPvRing], va);
+  constexpr bool kRead = B + kAhead < kPvBlocks;
+  if constexpr (kRead) v_reads_half<T, B + kAhead, 0>(ring[(B + kAhead) % kPvRing], va);
   MLA_SB();
-  (pv_mfma<B, J>(oacc, ring[B % kPvRing], pop, pay), ...);
+  pv_mfma<B, 0>(oacc, ring[B % kPvRing], pop, pay);
+  pv_mfma<B, 1>(oacc, ring[B % kPvRing], pop, pay);
+  pv_mfma<B, 2>(oacc, ring[B % kPvRing], pop, pay);
+  if constexpr (kRead) v_reads_half<T, B + kAhead, 1>(ring[(B + kAhead) % kPvRing], va);
+  MLA_SB();
+  pv_mfma<B, 3>(oacc, ring[B % kPvRing], pop, pay);
   if constexpr (B + 1 < kPvBlocks) {
     // reads issued after group B+1's: groups B+2 .. min(B+kAhead, last)
     constexpr int last = (B + kAhead < kPvBlocks) ? B + kAhead : kPvBlocks - 1;
@@ -1008,8 +1042,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
     auto prefetch_q = [&]() {
       if (cp + 1 == cend && it + 1 < total && cb < b_last) load_q(ncb);
     };
-#pragma unroll
-    for (int vt = 0; vt < kVTiles; ++vt) oacc[vt] = (f32x16){};
+    zero_acc(oacc);
     float m_run = -INFINITY, l_run = 0.f;
 
     // One page of the piece.  MASKED: some key of the page may be invisible to
@@ -1195,14 +1228,14 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
           weight2(sc1, ic<6>{});
         }
         pop[0] = __builtin_bit_cast(bf16x8, (u32x4){pk[0], pk[1], pk[2], pk[3]});
-        // weights of keys 16..31 in slots 0, 4, 8, 12 (used from MFMA 16 on)
+        // weights of keys 16..31 in slots 1, 5, 9, 13 (used from MFMA 16 on)
         auto pay_pv1 = [&](auto slot) {
           constexpr int k = decltype(slot)::value;
-          if constexpr (k < 16 && k % 4 == 0) {
-            weight2(sc1, ic<k / 2 + 8>{});
-            if constexpr (k == 12)
+          if constexpr (k < 16 && k % 4 == 1) {
+            weight2(sc1, ic<(k - 1) / 2 + 8>{});
+            if constexpr (k == 13)
               pop[1] = __builtin_bit_cast(bf16x8, (u32x4){pk[4], pk[5], pk[6], pk[7]});
-          } else if constexpr (k == 13) {
+          } else if constexpr (k == 14) {
             fold_ls();
           } else if constexpr (k == 17) {
             next_range(it + 2 < total);  // page it + 2, loaded during page it + 1
