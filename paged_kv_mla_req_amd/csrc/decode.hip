@@ -1022,6 +1022,14 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
   // for before that piece's output stores: vector memory operations complete
   // in order, so queries loaded after the stores would wait for them.
   bool first_wait = true;
+  // Lane offsets and lane id into the first KiB of the wave's staging area
+  // (again after each piece's output, which uses that area).
+  auto park_offsets = [&]() {
+    const uint32_t pl = pinned_lane();
+    const LaneOffsets o = lane_offsets(pl, wave);
+    *reinterpret_cast<u32x4*>(stage_all[wave] + 16 * pl) = (u32x4){o.k, o.v, o.load, pl};
+  };
+  park_offsets();
   load_q(cb);
   while (true) {
     // ---- one piece: pages [cp, cend) of request cb ---------------------------
@@ -1055,11 +1063,14 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
       // vmcnt(0): this wave's loads of page `it` landed (for a piece's first
       // page after the first piece: waited for before the previous epilogue);
       // the barrier: every wave's, and buffer it+1 is free again
+      // this lane's LDS offsets and id, kept in the wave's staging area: read
+      // before the barrier, so that the read's latency overlaps the wait
+      const u32x4 lov = *reinterpret_cast<const u32x4*>(stage_all[wave] + 16 * lane_id());
       if (first_wait) __builtin_amdgcn_s_waitcnt(0x0f70);
       first_wait = true;
       __syncthreads();
-      const uint32_t plane = pinned_lane();
-      const LaneOffsets lo = lane_offsets(plane, wave);
+      const uint32_t plane = lov[3];
+      const LaneOffsets lo = {lov[0], lov[1], lov[2]};
       const lds_u8* base = LDS_PTR(uint8_t, smem) + (FP8 ? 0 : (it & 1) * kPageBytes);
       // The next page's loads are spread over the MFMA work (issued back to
       // back they would stall the wave until the address unit drains them).
@@ -1288,6 +1299,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
       }
     }
     if (!more) break;
+    park_offsets();
     cb = ncb;
     cp = 0;
     piece = 0;
