@@ -170,6 +170,41 @@ def cpu_baseline(w, runs: int) -> dict:
             "seconds_per_pass": round(t, 4)}
 
 
+def time_append(mla, torch, w, p, reps: int) -> dict:
+    """mla_set_kv_buffer timed with events around `reps` back-to-back launches
+    (one at a time, kernel-sized work): the step's new tokens (the last q_len
+    of each request) and a 32768-token chunk at random distinct pool slots.
+    Bytes per token: the 1152-byte bf16 row read, its 8-byte slot, and the
+    1152 (bf16) or 576 (e4m3) bytes written."""
+    rng = np.random.default_rng(4242)
+    slots_step = np.array([w.req_to_token[int(w.req_pool_indices[b]), int(w.seq_lens[b]) - w.q_len + i]
+                           for b in range(w.bs) for i in range(w.q_len)], dtype=np.int64)
+    pool_slots = p.kv.shape[0] * 64
+    chunk = min(32768, pool_slots)
+    slots_chunk = rng.permutation(pool_slots)[:chunk].astype(np.int64)
+    res = {}
+    scale = None if w.kv_dtype == "bf16" else torch.tensor([1.0 / 64], dtype=torch.float32,
+                                                            device="cuda")
+    for name, sl in (("step", slots_step), ("chunk", slots_chunk)):
+        n = sl.size
+        k = torch.randn((n, 576), device="cuda").to(torch.bfloat16)
+        loc = torch.from_numpy(sl).cuda()
+        for _ in range(3):
+            mla.set_kv_buffer(p.kv, loc, k, kv_dtype=w.kv_dtype, kv_scale=scale)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            mla.set_kv_buffer(p.kv, loc, k, kv_dtype=w.kv_dtype, kv_scale=scale)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        per_tok = 1152 + 8 + (1152 if w.kv_dtype == "bf16" else 576)
+        res[name] = {"tokens": int(n), "us": round(ms * 1e3, 3),
+                     "gbs": round(n * per_tok / (ms * 1e-3) / 1e9, 2)}
+    return res
+
+
 def main() -> int:
     a = _args()
     if a.traffic_from:
@@ -318,6 +353,9 @@ def main() -> int:
     ms_dm = timed_loop(lambda i: (decode(pools[i % len(pools)]),
                                   mla.merge_states(po, pl, split_indptr, out, lse)), a.steps)
     ms_tp = timed_loop(lambda i: table_and_plan(pools[i % len(pools)]), a.steps)
+    # The KV append that precedes attention (set_kv_buffer): the step's new
+    # tokens, then a 32768-token chunk.  It writes into pool 0, so it runs last.
+    append = time_append(mla, torch, w, pools[0], a.steps)
 
     b = _algorithmic_bytes(w)
     kv_gbs = b["kv"] / (ms_step * 1e-3) / 1e9
@@ -354,6 +392,7 @@ def main() -> int:
         "ms_decode_merge": round(ms_dm, 5),
         "kv_read_gbs_decode_merge": round(b["kv"] / (ms_dm * 1e-3) / 1e9, 2),
         "ms_table_and_plan": round(ms_tp, 5),
+        "append": append,
         "step_launch": "hip graph replay" if a.graph else "eager",
         "ms_per_step_eager": None if ms_step_eager is None else round(ms_step_eager, 5),
         "roofline": {

@@ -251,6 +251,41 @@ mla_status mla_merge_states(const float* partial_o, const float* partial_lse,
                             const int32_t* split_indptr, int32_t bs, int32_t rows_per_req,
                             void* out, float* lse, hipStream_t stream);
 
+/*
+ * mla_set_kv_buffer — store the new tokens' latent rows in the paged cache
+ * (token_to_kv_pool.set_kv_buffer(layer, cache_loc, k, v) with
+ * cache_loc = out_cache_loc, which forward_decode and the target-verify
+ * branch of forward_extend on the FlashMLA page call before attention).
+ *
+ * For i < num_tokens and s = out_cache_loc[i] with 0 <= s < 64*num_pages,
+ * latent row i of k goes to row s % 64 of page s / 64.  In MLA V is the first
+ * 512 columns of that row, so nothing else is stored.  Slots outside the pool
+ * are skipped (never written).  Slots are expected to be distinct; if two
+ * tokens name one slot, which row it ends up holding is unspecified.
+ *
+ *   k              bf16 [num_tokens, k_row_stride], the first 576 columns of a
+ *                  row are its latent row; 16-byte aligned
+ *   k_row_stride   elements between rows, >= 576 and a multiple of 8
+ *   out_cache_loc  int64 [num_tokens] pool slots
+ *   kv_cache       [num_pages, 64, 576] bf16, or e4m3fn bytes for
+ *                  MLA_KV_FP8_E4M3; 16-byte aligned; updated in place
+ *   kv_scale       fp8 only: device fp32 scalar (the page's k_scale).  The
+ *                  stored byte is the e4m3fn value nearest to k / kv_scale
+ *                  (the quotient rounded to fp32, ties to even, magnitudes
+ *                  above 448 saturating to 448, NaN to 0x7F/0xFF), so that
+ *                  byte * kv_scale, the value mla_decode reads with the same
+ *                  scale as kv_descale, approximates k.  Expected positive
+ *                  and finite.  Ignored for bf16 (may be NULL).
+ *
+ * num_tokens == 0 launches nothing (k and out_cache_loc may then be NULL).
+ * Errors: INVALID_ARGUMENT for null pointers, num_tokens < 0, num_pages <= 0,
+ * k_row_stride < 576, or fp8 with a NULL kv_scale; UNSUPPORTED for an unknown kv_dtype or misaligned k,
+ * k_row_stride or kv_cache.
+ */
+mla_status mla_set_kv_buffer(const void* k, int64_t k_row_stride, const int64_t* out_cache_loc,
+                             int32_t num_tokens, void* kv_cache, int32_t kv_dtype,
+                             int64_t num_pages, const float* kv_scale, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -244,3 +244,30 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
                kv_dtype=kv_dtype, kv_descale=kv_descale, causal=causal, stream=stream)
     merge_states(workspace[0], workspace[1], split_indptr, out, lse, stream=stream)
     return out, lse
+
+
+def set_kv_buffer(kv_cache: torch.Tensor, out_cache_loc: torch.Tensor, k: torch.Tensor, *,
+                  kv_dtype="bf16", kv_scale: Optional[torch.Tensor] = None,
+                  stream=None) -> None:
+    """Store latent rows ``k`` (bf16 [n, 576], or a row-strided view whose rows
+    start 16-byte aligned) at pool slots ``out_cache_loc`` (int64 [n]) of
+    ``kv_cache`` [pages, 64, 576], in place (mla_set_kv_buffer).  For an fp8
+    cache ``kv_scale`` is the device fp32 per-tensor scale."""
+    code = _kv_code(kv_dtype)
+    kv_ok = (torch.bfloat16, torch.int16, torch.uint16) if code == MLA_KV_BF16 else (
+        torch.uint8, torch.float8_e4m3fn)
+    _need(kv_cache, "kv_cache", kv_ok, 3)
+    if kv_cache.shape[1:] != (PAGE_SIZE, LATENT_DIM):
+        raise ValueError(f"kv_cache must be [pages, 64, 576], got {tuple(kv_cache.shape)}")
+    _need(out_cache_loc, "out_cache_loc", (torch.int64,), 1)
+    if not isinstance(k, torch.Tensor) or not k.is_cuda or k.dtype != torch.bfloat16:
+        raise TypeError("k must be a bf16 GPU tensor")
+    if k.dim() != 2 or k.shape[1] != LATENT_DIM or k.stride(1) != 1:
+        raise ValueError("k must be [n, 576] with unit column stride")
+    if k.shape[0] != out_cache_loc.shape[0]:
+        raise ValueError("k and out_cache_loc disagree on the token count")
+    if kv_scale is not None:
+        _need(kv_scale, "kv_scale", (torch.float32,))
+    _lib.check(_lib.lib().mla_set_kv_buffer(
+        _p(k), k.stride(0) if k.shape[0] > 1 else LATENT_DIM, _p(out_cache_loc), k.shape[0],
+        _p(kv_cache), code, kv_cache.shape[0], _p(kv_scale), _stream(stream)))

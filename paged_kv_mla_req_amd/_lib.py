@@ -43,6 +43,7 @@ SIGNATURES = {
                             _c_p, _c_p, _c_p]),
     "mla_merge_states": (_c_i32, [_c_p, _c_p, _c_p, _c_i32, _c_i32, _c_p, _c_p, _c_p]),
     "mla_decode_time_next_launch": (_c_i32, [_c_p, _c_p]),
+    "mla_set_kv_buffer": (_c_i32, [_c_p, _c_i64, _c_p, _c_i32, _c_p, _c_i32, _c_i64, _c_p, _c_p]),
 }
 
 _lib = None

@@ -125,3 +125,29 @@ def test_table_and_plan_argument_errors():
     assert call(parts=600) == _lib.MLA_ERR_CAPACITY
     assert call(dtype=5) == _lib.MLA_ERR_INVALID_ARGUMENT
     assert _lib.lib().mla_last_error_message().startswith(b"mla_build_table_and_plan")
+
+
+def test_set_kv_buffer_argument_errors():
+    f = _lib.lib().mla_set_kv_buffer
+    ok = dict(k=FAKE, stride=576, loc=FAKE, n=4, kv=FAKE, dtype=0, pages=8, scale=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["k"], a["stride"], a["loc"], a["n"], a["kv"], a["dtype"], a["pages"],
+                 a["scale"], None)
+
+    assert call(k=None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert call(loc=None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert call(kv=None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert call(n=-1) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert call(pages=0) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert call(stride=575) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert call(dtype=1) == _lib.MLA_ERR_INVALID_ARGUMENT     # fp8 without a scale
+    assert call(dtype=9) == _lib.MLA_ERR_UNSUPPORTED
+    assert call(stride=580) == _lib.MLA_ERR_UNSUPPORTED       # not a multiple of 8
+    assert call(k=P(0x1008)) == _lib.MLA_ERR_UNSUPPORTED      # k not 16-byte aligned
+    assert _lib.lib().mla_last_error_message().startswith(b"mla_set_kv_buffer")
+    assert call(n=0) == _lib.MLA_OK                           # nothing to store: no launch
+    assert call(n=0, k=None, loc=None) == _lib.MLA_OK         # nothing is read then
+    assert call(n=0, kv=None) == _lib.MLA_ERR_INVALID_ARGUMENT
