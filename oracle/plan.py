@@ -159,3 +159,58 @@ def check_plan(table, indptr, seq_lens, num_parts: int, rows_per_req: int) -> No
         assert k == len(pieces_seen[b]), f"request {b}: {k} pieces declared, {len(pieces_seen[b])} found"
         for j, (_, idx, _, _) in enumerate(pieces_seen[b]):
             assert idx == j, f"request {b}: piece numbering"
+
+
+# ------------------------------------------------------------ fixed-size tiles
+
+def plan_fixed(seq_lens, tile_pages: int, max_parts: int):
+    """Deterministic plan with fixed-size tiles (the FlashInfer backend page's
+    deterministic mode: with enable_deterministic the decode KV is split into
+    tiles of decode_split_tile_size = 2048 tokens, and graph-mode KV splitting
+    is switched off).  Every request is cut at the multiples of ``tile_pages``
+    pages of its own sequence, so where it is cut does not depend on the rest
+    of the batch.
+
+    Request b has N_b = ceil(L_b / 64) pages and n_b = ceil(N_b / tile_pages)
+    pieces; split_indptr is the running sum of n_b.  Piece k of request b is
+    part split_indptr[b] + k, row (b, k*T, b, min((k+1)*T, N_b), k, pages, 0, 0),
+    T = tile_pages.  Rows from split_indptr[bs] to max_parts - 1 are zeros.
+    If the pieces do not fit in max_parts, nothing is planned: every row and
+    every split_indptr entry is 0 (so each request then has no piece).
+    """
+    L = np.asarray(seq_lens, dtype=np.int64)
+    bs = len(L)
+    T = int(tile_pages)
+    npages = -(-L // PAGE_SIZE)
+    pieces = -(-npages // T)
+    indptr = np.zeros(bs + 1, dtype=np.int64)
+    indptr[1:] = np.cumsum(pieces)
+    table = np.zeros((max_parts, 8), dtype=np.int32)
+    if indptr[-1] > max_parts:
+        return table, np.zeros(bs + 1, dtype=np.int32)
+    for b in range(bs):
+        for k in range(int(pieces[b])):
+            pg0, pg1 = k * T, min((k + 1) * T, int(npages[b]))
+            table[indptr[b] + k] = (b, pg0, b, pg1, k, pg1 - pg0, 0, 0)
+    return table, indptr.astype(np.int32)
+
+
+def check_fixed_plan(table, indptr, seq_lens, tile_pages: int) -> None:
+    """Raise AssertionError unless (table, indptr) covers every page of every
+    request exactly once, in order, by pieces that each lie inside one request,
+    start at a multiple of ``tile_pages`` pages and hold at most that many."""
+    table = np.asarray(table)
+    indptr = np.asarray(indptr, dtype=np.int64)
+    L = np.asarray(seq_lens, dtype=np.int64)
+    npages = -(-L // PAGE_SIZE)
+    assert indptr[0] == 0 and np.all(np.diff(indptr) >= 0)
+    for b in range(len(L)):
+        covered = 0
+        for k in range(int(indptr[b]), int(indptr[b + 1])):
+            b0, pg0, b1, pg1, idx, npg, r0, r1 = [int(v) for v in table[k]]
+            assert b0 == b1 == b and idx == k - indptr[b] and r0 == r1 == 0
+            assert pg0 == covered and pg0 % tile_pages == 0
+            assert 0 < npg == pg1 - pg0 <= tile_pages
+            covered = pg1
+        assert covered == npages[b]
+    assert not np.any(table[int(indptr[-1]):])

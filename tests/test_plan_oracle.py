@@ -68,3 +68,64 @@ def test_check_plan_rejects_broken_plans(what):
     bt, bip = _broken(t, ip, what)
     with pytest.raises(AssertionError):
         oracle.check_plan(bt, bip, lens, 256, 128)
+
+
+# ------------------------------------------------------------ fixed-size tiles
+
+def _pieces_by_page(lens, T):
+    """Brute force: page p of request b belongs to piece p // T of b."""
+    out = []
+    for b, L in enumerate(lens):
+        n = -(-int(L) // 64)
+        pieces = {}
+        for p in range(n):
+            pieces.setdefault(p // T, []).append(p)
+        out.append([(b, pg[0], pg[-1] + 1) for _, pg in sorted(pieces.items())])
+    return out
+
+
+@pytest.mark.parametrize("lens", [[1], [0], [64 * 32], [64 * 32 + 1], [37, 130], [0, 5, 0, 700],
+                                  [2048, 2049, 4095, 4096, 4097, 1]])
+@pytest.mark.parametrize("T", [1, 4, 32])
+def test_fixed_plan_matches_page_enumeration(lens, T):
+    bf = _pieces_by_page(lens, T)
+    need = sum(len(x) for x in bf)
+    t, ip = oracle.plan_fixed(lens, T, max(need, 1) + 3)
+    oracle.check_fixed_plan(t, ip, lens, T)
+    got = [[(int(r[0]), int(r[1]), int(r[3])) for r in t[ip[b]:ip[b + 1]]] for b in range(len(lens))]
+    assert got == bf
+
+
+@pytest.mark.parametrize("name", sorted(CONFIGS))
+def test_fixed_plan_on_named_workloads_and_batch_invariance(name):
+    lens = workload_seq_lens(name)
+    T = 32                                  # 2048 tokens, the page's default tile
+    need = int(sum(-(-(-(-int(L) // 64)) // T) for L in lens))
+    t, ip = oracle.plan_fixed(lens, T, need)
+    oracle.check_fixed_plan(t, ip, lens, T)
+    # A request's pieces do not depend on the rest of the batch: plan request 1
+    # alone, and inside a reversed batch, and compare its rows (request field aside).
+    b = min(1, len(lens) - 1)
+    cols = [1, 3, 4, 5, 6, 7]                # every field but the request index
+    mine = t[ip[b]:ip[b + 1]][:, cols]
+    t1, ip1 = oracle.plan_fixed(lens[b:b + 1], T, need)
+    assert np.array_equal(mine, t1[ip1[0]:ip1[1]][:, cols])
+    rb = len(lens) - 1 - b
+    t2, ip2 = oracle.plan_fixed(lens[::-1], T, need)
+    assert np.array_equal(mine, t2[ip2[rb]:ip2[rb + 1]][:, cols])
+
+
+def test_fixed_plan_overflow_plans_nothing_and_checker_catches_mutations():
+    lens = [4096, 100, 70000]
+    t, ip = oracle.plan_fixed(lens, 4, 5)           # needs 16 + 1 + 274 pieces
+    assert not t.any() and not ip.any()
+    t, ip = oracle.plan_fixed(lens, 4, 400)
+    oracle.check_fixed_plan(t, ip, lens, 4)
+    for mutate in (lambda a: a.__setitem__((0, 3), a[0, 3] + 1),     # overlaps piece 1
+                   lambda a: a.__setitem__((1, 1), a[1, 1] + 1),     # gap, off the grid
+                   lambda a: a.__setitem__((0, 4), 3),               # wrong piece index
+                   lambda a: a.__setitem__((300, 5), 1)):            # junk past the end
+        bad = t.copy()
+        mutate(bad)
+        with pytest.raises(AssertionError):
+            oracle.check_fixed_plan(bad, ip, lens, 4)
