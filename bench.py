@@ -50,6 +50,11 @@ def _args():
                     help="time replays of the step captured in a HIP graph (measured slower than "
                          "eager launches here: the four launches are not host-bound)")
     ap.add_argument("--cpu-runs", type=int, default=3)
+    ap.add_argument("--plan", choices=("balanced", "fixed"), default="balanced",
+                    help="balanced: one cost-balanced part per CU (default); fixed: the "
+                         "deterministic fixed-tile plan (batch-invariant results)")
+    ap.add_argument("--tile-pages", type=int, default=32,
+                    help="pages per tile of the fixed plan (32 = 2048 tokens)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before warm-up, run one plain elementwise kernel (bitwise not) that "
                          "reads and writes this many MiB: the known-size reference for HBM "
@@ -240,14 +245,17 @@ def main() -> int:
     R = w.rows_per_req
     width = w.bt_width
     cus = mla.device_num_cus()
+    max_len = int(w.seq_lens.max())
     num_parts = cus
+    if a.plan == "fixed":
+        num_parts = max(1, int(mla._lib.lib().mla_fixed_split_parts_bound(w.bs, max_len,
+                                                                         a.tile_pages)))
     bt = torch.empty((w.bs, width), dtype=torch.int32, device="cuda")
     tile_plan = torch.empty((num_parts, 8), dtype=torch.int32, device="cuda")
     split_indptr = torch.empty((w.bs + 1,), dtype=torch.int32, device="cuda")
     po, pl = mla.partial_buffers(w.bs, R, num_parts)
     out = torch.empty((w.bs, w.q_len, w.heads, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((w.bs, w.q_len, w.heads), dtype=torch.float32, device="cuda")
-    max_len = int(w.seq_lens.max())
     # For every EV_EVERY-th timed step, a pair of events that the decode
     # kernel's own launch records at its begin and end
     # (mla_decode_time_next_launch).  An event-recorded launch ends with a
@@ -266,6 +274,12 @@ def main() -> int:
                        kv_descale=p.kv_descale, causal=w.causal)
 
     def table_and_plan(p):
+        if a.plan == "fixed":
+            mla.build_block_table(p.req_to_token, p.req_pool_indices, p.seq_lens, width,
+                                  max_seq_len_hint=max_len, out=bt)
+            mla.plan_fixed_splits(p.seq_lens, a.tile_pages, num_parts, max_seq_len_hint=max_len,
+                                  tile_plan=tile_plan, split_indptr=split_indptr)
+            return
         mla.build_table_and_plan(p.req_to_token, p.req_pool_indices, p.seq_lens, width, R,
                                  num_parts, w.kv_dtype, max_seq_len_hint=max_len, out=bt,
                                  tile_plan=tile_plan, split_indptr=split_indptr)
@@ -384,6 +398,7 @@ def main() -> int:
             "seq_len": int(round(float(w.seq_lens.mean()))),
             "parallelism": "single GPU",
             "num_parts": num_parts,
+            "plan": a.plan if a.plan == "balanced" else f"fixed tiles of {a.tile_pages} pages",
             "kv_pools_rotated": len(pools),
         },
         "pct_hbm_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),

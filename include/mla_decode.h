@@ -48,6 +48,7 @@ extern "C" {
 #define MLA_MAX_ROWS_PER_REQ 512   /* H * q_len */
 #define MLA_MAX_BATCH 16384        /* planner limit */
 #define MLA_MAX_PARTS 512          /* planner limit (also <= device CU count) */
+#define MLA_MAX_DECODE_PARTS 65536 /* parts one mla_decode launch takes (fixed-tile plans) */
 
 typedef enum mla_status {
   MLA_OK = 0,
@@ -140,6 +141,46 @@ mla_status mla_plan_splits(const int32_t* seq_lens, int32_t bs, int32_t rows_per
                            int32_t* split_indptr, hipStream_t stream);
 
 /*
+ * mla_plan_fixed_splits — deterministic plan with fixed-size tiles (the
+ * FlashInfer backend page's deterministic mode: enable_deterministic splits
+ * the decode KV into tiles of decode_split_tile_size = 2048 tokens, i.e. 32
+ * pages, and switches graph-mode KV splitting off).
+ *
+ * Request b, with N_b = ceil(seq_lens[b] / 64) pages, is cut at the
+ * multiples of tile_pages pages of its own sequence into
+ * n_b = ceil(N_b / tile_pages) pieces.  Where a request is cut, and so every
+ * floating-point step of its result, does not depend on the other requests
+ * of the batch or on max_parts: a request decodes bit for bit the same alone
+ * or in any batch.  Each part holds exactly one piece:
+ *   split_indptr[b] = n_0 + ... + n_{b-1},
+ *   part split_indptr[b] + k = {b, k*T, b, min((k+1)*T, N_b), k, pages, 0, 0}
+ * (the mla_plan_splits row format), T = tile_pages; rows from
+ * split_indptr[bs] to max_parts - 1 are zeros (parts with nothing to do).
+ * Pass the plan to mla_decode with num_parts = max_parts and
+ * partial_slots >= bs + max_parts.  Unlike mla_plan_splits, the number of
+ * parts is not tied to the CU count, so short batches may leave CUs idle.
+ *
+ *   tile_plan         int32 [max_parts, 8], 16-byte aligned
+ *   split_indptr      int32 [bs + 1]
+ *   max_seq_len_hint  host: an upper bound of seq_lens, or -1
+ *
+ * If the pieces do not fit in max_parts rows (possible only without a
+ * hint), nothing is planned: every row and every split_indptr entry is 0, so
+ * decode and merge then write o = 0 and lse = -inf for every row.
+ *
+ * Errors: INVALID_ARGUMENT for null pointers or bs, tile_pages or max_parts
+ * <= 0; CAPACITY for bs > MLA_MAX_BATCH, max_parts > MLA_MAX_DECODE_PARTS,
+ * or when the hint allows more pieces than max_parts
+ * (mla_fixed_split_parts_bound(bs, hint, tile_pages) > max_parts).
+ */
+mla_status mla_plan_fixed_splits(const int32_t* seq_lens, int32_t bs, int32_t tile_pages,
+                                 int32_t max_parts, int32_t max_seq_len_hint,
+                                 int32_t* tile_plan, int32_t* split_indptr, hipStream_t stream);
+/* Host helper: bs * ceil(ceil(max_seq_len / 64) / tile_pages), the most
+ * pieces a fixed-tile plan of such a batch can have (INT32_MAX if larger;
+ * -1 for negative sizes or tile_pages <= 0). */
+int32_t mla_fixed_split_parts_bound(int32_t bs, int32_t max_seq_len, int32_t tile_pages);
+/*
  * mla_build_table_and_plan — mla_build_block_table and mla_plan_splits in
  * one launch (init_forward_metadata of both page backends computes the block
  * table and the split metadata together, once per batch step).  One work-group
@@ -208,7 +249,7 @@ int32_t mla_device_num_cus(void);
  * Errors: INVALID_ARGUMENT for null pointers, non-positive sizes, a
  * negative or non-finite scale, or fp8 with a NULL kv_descale; UNSUPPORTED for
  * q_len*num_heads outside 1..512 or an unknown kv_dtype; CAPACITY when
- * partial_slots < bs + num_parts.
+ * partial_slots < bs + num_parts or num_parts > MLA_MAX_DECODE_PARTS.
  */
 mla_status mla_decode(const void* q, int32_t bs, int32_t q_len, int32_t num_heads,
                       const void* kv_cache, int32_t kv_dtype, int64_t num_pages,

@@ -110,6 +110,36 @@ def plan_splits(seq_lens: torch.Tensor, rows_per_req: int, num_parts: Optional[i
     return tile_plan[:num_parts], split_indptr[:bs + 1]
 
 
+def plan_fixed_splits(seq_lens: torch.Tensor, tile_pages: int = 32,
+                      max_parts: Optional[int] = None, max_seq_len_hint: int = -1,
+                      tile_plan: Optional[torch.Tensor] = None,
+                      split_indptr: Optional[torch.Tensor] = None,
+                      stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Deterministic fixed-tile plan (mla_plan_fixed_splits): every request cut at
+    multiples of ``tile_pages`` pages (default 32 = 2048 tokens).  ``max_parts``
+    defaults to the bound for ``max_seq_len_hint``, which is then required.
+    Returns (tile_plan int32 [max_parts, 8], split_indptr int32 [bs + 1])."""
+    _need(seq_lens, "seq_lens", (torch.int32,), 1)
+    bs = seq_lens.shape[0]
+    if max_parts is None:
+        if max_seq_len_hint < 0:
+            raise ValueError("plan_fixed_splits needs max_parts or max_seq_len_hint")
+        max_parts = max(1, int(_lib.lib().mla_fixed_split_parts_bound(bs, max_seq_len_hint,
+                                                                       tile_pages)))
+    if tile_plan is None:
+        tile_plan = torch.empty((max_parts, 8), dtype=torch.int32, device=seq_lens.device)
+    if split_indptr is None:
+        split_indptr = torch.empty((bs + 1,), dtype=torch.int32, device=seq_lens.device)
+    _need(tile_plan, "tile_plan", (torch.int32,), 2)
+    _need(split_indptr, "split_indptr", (torch.int32,), 1)
+    if tile_plan.shape != (max_parts, 8) or split_indptr.shape != (bs + 1,):
+        raise ValueError("tile_plan must be [max_parts, 8] and split_indptr [bs + 1]")
+    _lib.check(_lib.lib().mla_plan_fixed_splits(_p(seq_lens), bs, tile_pages, max_parts,
+                                                max_seq_len_hint, _p(tile_plan),
+                                                _p(split_indptr), _stream(stream)))
+    return tile_plan, split_indptr
+
+
 def build_table_and_plan(req_to_token: torch.Tensor, req_pool_indices: torch.Tensor,
                          seq_lens: torch.Tensor, width: int, rows_per_req: int,
                          num_parts: Optional[int] = None, kv_dtype="bf16", pad_value: int = -1,

@@ -35,6 +35,8 @@ SIGNATURES = {
     "mla_build_table_and_plan": (_c_i32, [_c_p, _c_i32, _c_i64, _c_p, _c_p, _c_i32, _c_i32, _c_p,
                                           _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_p,
                                           _c_p, _c_p]),
+    "mla_plan_fixed_splits": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_p, _c_p]),
+    "mla_fixed_split_parts_bound": (_c_i32, [_c_i32, _c_i32, _c_i32]),
     "mla_max_total_splits": (_c_i32, [_c_i32, _c_i32]),
     "mla_partial_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32]),
     "mla_device_num_cus": (_c_i32, []),

@@ -1353,8 +1353,9 @@ extern "C" mla_status mla_decode(const void* q, int32_t bs, int32_t q_len, int32
   const int64_t rows = (int64_t)q_len * num_heads;
   if (rows < 1 || rows > MLA_MAX_ROWS_PER_REQ)
     return fail(MLA_ERR_UNSUPPORTED, "mla_decode: q_len*num_heads must be in 1..512");
-  if (num_parts > MLA_MAX_PARTS)
-    return fail(MLA_ERR_CAPACITY, "mla_decode: num_parts above " + std::to_string(MLA_MAX_PARTS));
+  if (num_parts > MLA_MAX_DECODE_PARTS)
+    return fail(MLA_ERR_CAPACITY,
+                "mla_decode: num_parts above " + std::to_string(MLA_MAX_DECODE_PARTS));
   if ((int64_t)partial_slots < (int64_t)bs + num_parts)
     return fail(MLA_ERR_CAPACITY, "mla_decode: partial_slots must be at least bs + num_parts");
 

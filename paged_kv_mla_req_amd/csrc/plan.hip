@@ -509,3 +509,102 @@ extern "C" mla_status mla_build_table_and_plan(
                      plan_overhead_q(rows_per_req), num_parts, tile_plan, split_indptr);
   return check_launch(who);
 }
+
+// ---------------------------------------------------------------------------
+// Fixed-tile planner (the FlashInfer backend page's deterministic mode: with
+// enable_deterministic the decode KV is split into tiles of
+// decode_split_tile_size = 2048 tokens and graph-mode KV splitting is off).
+// Request b is cut at the multiples of tile_pages pages of its own sequence,
+// so its pieces -- and so the arithmetic of its result -- do not depend on
+// the rest of the batch.  Piece k of request b is part split_indptr[b] + k.
+// One work-group: two passes of block scans over chunks of 256 requests (the
+// first only counts), then the rows past the last piece are cleared.
+namespace mla {
+
+__device__ __forceinline__ int fixed_pieces(int32_t L, int tile_pages, int cap) {
+  const int np = L > 0 ? (L >> 6) + ((L & (kPage - 1)) != 0) : 0;
+  return min(np / tile_pages + (np % tile_pages != 0), cap);
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_fixed_kernel(
+    const int32_t* __restrict__ seq_lens, int32_t bs, int32_t tile_pages, int32_t max_parts,
+    int32_t* __restrict__ tile_plan, int32_t* __restrict__ split_indptr) {
+  __shared__ int wave_tot[kPlanWaves];
+  // A request's count is capped at max_parts + 1: the sum of at most 16384
+  // capped counts fits an int, and any capped request already overflows.
+  const int cap = max_parts + 1;
+  int total = 0;
+  for (int c0 = 0; c0 < bs; c0 += kPlanThreads) {
+    const int b = c0 + (int)threadIdx.x;
+    const int n = b < bs ? fixed_pieces(seq_lens[b], tile_pages, cap) : 0;
+    int chunk_total;
+    block_exclusive_scan(n, wave_tot, &chunk_total);
+    total = min(total + chunk_total, cap);
+  }
+  const bool fits = total <= max_parts;
+  int base = 0;
+  for (int c0 = 0; fits && c0 < bs; c0 += kPlanThreads) {
+    const int b = c0 + (int)threadIdx.x;
+    const int n = b < bs ? fixed_pieces(seq_lens[b], tile_pages, cap) : 0;
+    int chunk_total;
+    const int before = base + block_exclusive_scan(n, wave_tot, &chunk_total);
+    if (b < bs) {
+      split_indptr[b] = before;
+      const int np = seq_lens[b] > 0 ? (seq_lens[b] >> 6) + ((seq_lens[b] & (kPage - 1)) != 0)
+                                     : 0;
+      for (int k = 0; k < n; ++k) {
+        const int pg0 = k * tile_pages, pg1 = min(pg0 + tile_pages, np);
+        int32_t* row = tile_plan + (int64_t)(before + k) * 8;
+        *reinterpret_cast<int4*>(row) = make_int4(b, pg0, b, pg1);
+        *reinterpret_cast<int4*>(row + 4) = make_int4(k, pg1 - pg0, 0, 0);
+      }
+    }
+    base += chunk_total;
+  }
+  // Without room, nothing is planned: split_indptr and every row are 0.
+  const int used = fits ? total : 0;
+  if (!fits)
+    for (int b = (int)threadIdx.x; b < bs; b += kPlanThreads) split_indptr[b] = 0;
+  if (threadIdx.x == 0) split_indptr[bs] = used;
+  for (int64_t i = (int64_t)used * 8 + threadIdx.x; i < (int64_t)max_parts * 8; i += kPlanThreads)
+    tile_plan[i] = 0;
+}
+
+// ceil(ceil(max_seq_len / 64) / tile_pages) pieces per request, times bs;
+// -1 for bad arguments, INT32_MAX when the count does not fit.
+int64_t fixed_parts_bound(int32_t bs, int32_t max_seq_len, int32_t tile_pages) {
+  if (bs < 0 || max_seq_len < 0 || tile_pages <= 0) return -1;
+  const int64_t np = ((int64_t)max_seq_len + kPage - 1) / kPage;
+  return (int64_t)bs * ((np + tile_pages - 1) / tile_pages);
+}
+
+}  // namespace mla
+
+extern "C" int32_t mla_fixed_split_parts_bound(int32_t bs, int32_t max_seq_len,
+                                               int32_t tile_pages) {
+  const int64_t v = mla::fixed_parts_bound(bs, max_seq_len, tile_pages);
+  return v > INT32_MAX ? INT32_MAX : (int32_t)v;
+}
+
+extern "C" mla_status mla_plan_fixed_splits(const int32_t* seq_lens, int32_t bs,
+                                            int32_t tile_pages, int32_t max_parts,
+                                            int32_t max_seq_len_hint, int32_t* tile_plan,
+                                            int32_t* split_indptr, hipStream_t stream) {
+  using namespace mla;
+  const std::string w("mla_plan_fixed_splits");
+  if (!seq_lens || !tile_plan || !split_indptr)
+    return fail(MLA_ERR_INVALID_ARGUMENT, w + ": null pointer");
+  if (bs <= 0 || tile_pages <= 0 || max_parts <= 0)
+    return fail(MLA_ERR_INVALID_ARGUMENT, w + ": bs, tile_pages and max_parts must be positive");
+  if (bs > MLA_MAX_BATCH)
+    return fail(MLA_ERR_CAPACITY, w + ": bs above " + std::to_string(MLA_MAX_BATCH));
+  if (max_parts > MLA_MAX_DECODE_PARTS)
+    return fail(MLA_ERR_CAPACITY, w + ": max_parts above " + std::to_string(MLA_MAX_DECODE_PARTS));
+  if (max_seq_len_hint >= 0 && fixed_parts_bound(bs, max_seq_len_hint, tile_pages) > max_parts)
+    return fail(MLA_ERR_CAPACITY, w + ": " + std::to_string(bs) + " requests of up to " +
+                                      std::to_string(max_seq_len_hint) +
+                                      " tokens may need more than max_parts pieces");
+  hipLaunchKernelGGL(plan_fixed_kernel, dim3(1), dim3(kPlanThreads), 0, stream, seq_lens, bs,
+                     tile_pages, max_parts, tile_plan, split_indptr);
+  return check_launch(w.c_str());
+}

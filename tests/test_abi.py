@@ -67,7 +67,7 @@ def _decode(**kw):
     (dict(heads=513), _lib.MLA_ERR_UNSUPPORTED),              # rows > 512
     (dict(q_len=5, heads=128), _lib.MLA_ERR_UNSUPPORTED),     # 640 rows
     (dict(slots=5), _lib.MLA_ERR_CAPACITY),                   # < bs + parts
-    (dict(parts=513, slots=600), _lib.MLA_ERR_CAPACITY),
+    (dict(parts=65537, slots=70000), _lib.MLA_ERR_CAPACITY),
 ])
 def test_decode_argument_errors(kw, status):
     assert _decode(**kw) == status
@@ -151,3 +151,21 @@ def test_set_kv_buffer_argument_errors():
     assert call(n=0) == _lib.MLA_OK                           # nothing to store: no launch
     assert call(n=0, k=None, loc=None) == _lib.MLA_OK         # nothing is read then
     assert call(n=0, kv=None) == _lib.MLA_ERR_INVALID_ARGUMENT
+
+
+def test_fixed_plan_argument_errors_and_bound():
+    lib = _lib.lib()
+    f = lib.mla_plan_fixed_splits
+    assert f(None, 2, 32, 8, -1, FAKE, FAKE, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert f(FAKE, 0, 32, 8, -1, FAKE, FAKE, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert f(FAKE, 2, 0, 8, -1, FAKE, FAKE, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert f(FAKE, 2, 32, 0, -1, FAKE, FAKE, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert f(FAKE, 20000, 32, 8, -1, FAKE, FAKE, None) == _lib.MLA_ERR_CAPACITY
+    assert f(FAKE, 2, 32, 65537, -1, FAKE, FAKE, None) == _lib.MLA_ERR_CAPACITY
+    # 2 requests of up to 4097 tokens = 65 pages = 3 tiles of 32 pages each: 6 > 5
+    assert f(FAKE, 2, 32, 5, 4097, FAKE, FAKE, None) == _lib.MLA_ERR_CAPACITY
+    assert lib.mla_last_error_message().startswith(b"mla_plan_fixed_splits")
+    b = lib.mla_fixed_split_parts_bound
+    assert b(2, 4097, 32) == 6 and b(64, 8192, 32) == 256 and b(3, 0, 32) == 0
+    assert b(1, 1, 1) == 1 and b(-1, 5, 32) == -1 and b(2, 5, 0) == -1
+    assert b(16384, 2**31 - 1, 1) == 2**31 - 1

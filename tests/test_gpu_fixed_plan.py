@@ -1,0 +1,132 @@
+"""GPU: the deterministic fixed-tile plan (mla_plan_fixed_splits).
+
+The plan is integer work and must equal the oracle's rule bit for bit; a
+decode over it must match the fp64 oracle within the parity tolerances; and a
+request must decode bit for bit the same alone, in another batch, or with
+another max_parts (the point of fixed tiles).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.test_gpu_parity import _np, _sample_rows, assert_close, ref
+from workloads import make_custom, make_workload, workload_seq_lens, CONFIGS
+from workloads.device import to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mla():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_mla_req_amd as m
+    return m
+
+
+def _need(lens, T):
+    return int(sum(-(-(-(-int(L) // 64)) // T) for L in lens))
+
+
+@pytest.mark.parametrize("lens,T,extra", [
+    ([37, 130], 1, 0), ([37, 130], 1, 5), ([0], 32, 1), ([1], 32, 0), ([2048, 2049, 4096], 32, 2),
+    ([0, 5, 0, 700], 4, 0), ("dsv3", 32, 0), ("long", 32, 0), ("verify", 32, 0),
+    ("fp8", 32, 7), ("dsv3", 8, 0), ("rand1000", 16, 3), ("many16384", 32, 0),
+])
+def test_fixed_plan_bit_exact(mla, lens, T, extra):
+    if lens == "rand1000":
+        lens = np.random.default_rng(3).integers(0, 20000, size=1000)
+    elif lens == "many16384":
+        lens = np.random.default_rng(4).integers(1, 200, size=16384)
+    elif isinstance(lens, str):
+        lens = workload_seq_lens(lens)
+    lens = np.asarray(lens, dtype=np.int32)
+    max_parts = max(1, _need(lens, T) + extra)
+    sl = torch.from_numpy(lens).cuda()
+    t, ip = mla.plan_fixed_splits(sl, T, max_parts)
+    t_ref, ip_ref = oracle.plan_fixed(lens, T, max_parts)
+    assert np.array_equal(_np(t), t_ref)
+    assert np.array_equal(_np(ip), ip_ref)
+    oracle.check_fixed_plan(_np(t), _np(ip), lens, T)
+
+
+def test_fixed_plan_overflow_plans_nothing(mla):
+    lens = np.array([4096, 100, 70000], dtype=np.int32)
+    sl = torch.from_numpy(lens).cuda()
+    t, ip = mla.plan_fixed_splits(sl, 4, 5)            # no hint: the device finds 291 > 5
+    assert not _np(t).any() and not _np(ip).any()
+
+
+def _fixed_decode(mla, d, w, bt_width, T, max_parts, idx=None):
+    """Block table, fixed plan, decode and merge for the requests `idx` of w
+    (all by default), sharing w's pool and req_to_token."""
+    q, sl, rpi = d.q, d.seq_lens, d.req_pool_indices
+    if idx is not None:
+        ii = torch.as_tensor(idx, dtype=torch.long, device="cuda")
+        q, sl, rpi = q[ii].contiguous(), sl[ii].contiguous(), rpi[ii].contiguous()
+    bt = mla.build_block_table(d.req_to_token, rpi, sl, bt_width)
+    plan = mla.plan_fixed_splits(sl, T, max_parts)
+    out, lse = mla.decode(q, d.kv, bt, sl, w.softmax_scale, kv_dtype=w.kv_dtype,
+                          kv_descale=d.kv_descale, causal=w.causal, plan=plan)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+CASES = [
+    dict(bs=2, heads=16, q_len=1, lens=[37, 130], T=1, kv="bf16"),
+    dict(bs=6, heads=128, q_len=1, lens=[100, 3000, 5000, 64, 2049, 777], T=4, kv="bf16"),
+    dict(bs=4, heads=16, q_len=4, lens=[5, 300, 1500, 4100], T=2, kv="bf16"),
+    dict(bs=3, heads=128, q_len=1, lens=[129, 2500, 4096], T=8, kv="fp8_e4m3"),
+]
+
+
+@pytest.mark.parametrize("c", CASES, ids=lambda c: f"b{c['bs']}h{c['heads']}n{c['q_len']}T{c['T']}{c['kv']}")
+def test_fixed_plan_decode_matches_oracle(mla, c):
+    w = make_custom("fixed", bs=c["bs"], heads=c["heads"], q_len=c["q_len"], seq_lens=c["lens"],
+                    seed=41, kv_dtype=c["kv"], value_scale=0.5)
+    d = to_device(w)
+    out, lse = _fixed_decode(mla, d, w, w.bt_width, c["T"], _need(c["lens"], c["T"]) + 2)
+    o_ref, lse_ref = ref(w)
+    assert_close(_np(out), _np(lse), o_ref, lse_ref)
+
+
+def test_fixed_plan_batch_invariance_bit_exact(mla):
+    """The same requests decoded in the whole batch, in a reordered sub-batch
+    and with more plan rows give bit-identical bf16 outputs and fp32 LSEs."""
+    lens = [100, 3000, 5000, 64, 2049, 777, 4097, 1]
+    w = make_custom("inv", bs=len(lens), heads=128, q_len=1, seq_lens=lens, seed=43,
+                    value_scale=0.5)   # short contexts: |o| < 4, so one bf16 rounding stays < 1e-2
+    d = to_device(w)
+    T = 4
+    out_a, lse_a = _fixed_decode(mla, d, w, w.bt_width, T, _need(lens, T))
+    idx = [6, 1, 2, 4]
+    sub = [lens[i] for i in idx]
+    out_b, lse_b = _fixed_decode(mla, d, w, w.bt_width + 3, T, _need(sub, T) + 9, idx=idx)
+    ii = torch.as_tensor(idx, device="cuda")
+    assert torch.equal(out_b.view(torch.int16), out_a[ii].view(torch.int16))
+    assert torch.equal(lse_b, lse_a[ii])
+    # and each request alone
+    for j, i in enumerate(idx):
+        out_c, lse_c = _fixed_decode(mla, d, w, w.bt_width, T, _need([lens[i]], T), idx=[i])
+        assert torch.equal(out_c.view(torch.int16), out_a[i:i + 1].view(torch.int16))
+        assert torch.equal(lse_c, lse_a[i:i + 1])
+    o_ref, lse_ref = ref(w)
+    assert_close(_np(out_a), _np(lse_a), o_ref, lse_ref)
+
+
+@pytest.mark.parametrize("name", ["dsv3", "verify", "fp8"])
+def test_fixed_plan_full_size_sampled_rows(mla, name):
+    """Full-size workloads with the page's 2048-token tiles (32 pages)."""
+    w = make_workload(name)
+    d = to_device(w)
+    T = 32
+    out, lse = _fixed_decode(mla, d, w, w.bt_width, T, _need(w.seq_lens, T))
+    rows = _sample_rows(w, 6, seed=1)
+    o_ref, lse_ref = ref(w, rows=rows)
+    mask = np.zeros((w.bs, w.q_len * w.heads), dtype=bool)
+    for b, r in rows.items():
+        mask[b, r] = True
+    mask = mask.reshape(w.bs, w.q_len, w.heads)
+    assert_close(_np(out), _np(lse), o_ref, lse_ref, mask=mask)
