@@ -130,3 +130,57 @@ def test_fixed_plan_full_size_sampled_rows(mla, name):
         mask[b, r] = True
     mask = mask.reshape(w.bs, w.q_len, w.heads)
     assert_close(_np(out), _np(lse), o_ref, lse_ref, mask=mask)
+
+
+def test_captured_append_and_fixed_plan_step_replays(mla):
+    """KV append, block table, fixed plan, decode and merge captured in one HIP
+    graph (the fixed plan's part count is fixed by the capacity, so the launch
+    shapes do not change between replays): every replay, with eager work and
+    synchronisation in between, equals the eager step bit for bit, and the
+    result matches the oracle's append + decode."""
+    from tests.test_gpu_append import _bf16_rows, _dev_u16
+
+    lens = [900, 130, 2000]
+    w = make_custom("graph_fixed", bs=3, heads=128, q_len=1, seq_lens=lens, seed=52,
+                    value_scale=0.5)
+    d = to_device(w)
+    rows, T = w.rows_per_req, 4
+    max_parts = _need(lens, T) + 3
+    slots = np.array([int(w.req_to_token[int(w.req_pool_indices[b]), lens[b] - 1])
+                      for b in range(w.bs)], dtype=np.int64)
+    k = _bf16_rows(np.random.default_rng(8), w.bs, 0.5)
+    loc, kd = torch.from_numpy(slots).cuda(), _dev_u16(k)
+    bt = torch.empty((w.bs, w.bt_width), dtype=torch.int32, device="cuda")
+    tp = torch.empty((max_parts, 8), dtype=torch.int32, device="cuda")
+    ip = torch.empty((w.bs + 1,), dtype=torch.int32, device="cuda")
+    po, pl = mla.partial_buffers(w.bs, rows, max_parts)
+    out = torch.empty((w.bs, 1, w.heads, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.bs, 1, w.heads), dtype=torch.float32, device="cuda")
+
+    def step():
+        mla.set_kv_buffer(d.kv, loc, kd)
+        mla.build_block_table(d.req_to_token, d.req_pool_indices, d.seq_lens, w.bt_width, out=bt)
+        mla.plan_fixed_splits(d.seq_lens, T, max_parts, tile_plan=tp, split_indptr=ip)
+        mla.mla_decode(d.q, d.kv, bt, d.seq_lens, tp, ip, w.softmax_scale, partial_o=po,
+                       partial_lse=pl, out=out, lse=lse)
+        mla.merge_states(po, pl, ip, out, lse)
+
+    step()
+    torch.cuda.synchronize()
+    ref_o, ref_l = out.clone(), lse.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        out.zero_()
+        lse.zero_()
+        po.zero_()
+        tp.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
+    kv_ref = oracle.set_kv_buffer(w.kv, slots, k, "bf16")
+    o_ref, lse_ref = oracle.paged_decode(w.q_bits, kv_ref, "bf16", 1.0, w.req_to_token,
+                                         w.req_pool_indices, w.seq_lens, w.softmax_scale, w.causal)
+    assert_close(_np(out), _np(lse), o_ref, lse_ref)
