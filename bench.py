@@ -30,6 +30,7 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure (no sparsity)
 EV_EVERY = 5     # timed steps per decode launch that records its own events
 SETTLE_S = 0.3   # default seconds of untimed steps before the warm-up steps
 
@@ -79,6 +80,39 @@ def _algorithmic_bytes(w) -> dict:
     lse = w.bs * R * 4
     bt = int((-(-L // 64)).sum()) * 4
     return dict(kv=kv, q=q, o=o, lse=lse, bt=bt, total=kv + q + o + lse + bt)
+
+
+def _algorithmic_flops(w) -> int:
+    """Matrix work of one pass: 2 flop per multiply-add of the scores (576
+    wide) and of the output (512 wide), per visible (row, key) pair; with
+    causal masking row i of q_len n sees L - n + i + 1 keys."""
+    L = w.seq_lens.astype(np.int64)
+    n = w.q_len
+    if w.causal:
+        vis = sum(int(np.clip(L - n + i + 1, 0, None).sum()) for i in range(n))
+    else:
+        vis = int(L.sum()) * n
+    return 2 * (576 + 512) * w.heads * vis
+
+
+def measured_copy_gbs(torch, mib: int = 2048, reps: int = 10) -> float:
+    """Device-to-device copy bandwidth on this machine (bytes read + written per
+    second), the practical ceiling an HBM-streaming kernel is compared with."""
+    n = mib << 18
+    src = torch.ones(n, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return 2 * (mib << 20) / (ms * 1e-3) / 1e9
 
 
 def _traffic_path(root: str, workload: str) -> str:
@@ -370,11 +404,14 @@ def main() -> int:
     # The KV append that precedes attention (set_kv_buffer): the step's new
     # tokens, then a 32768-token chunk.  It writes into pool 0, so it runs last.
     append = time_append(mla, torch, w, pools[0], a.steps)
+    copy_gbs = measured_copy_gbs(torch)
 
     b = _algorithmic_bytes(w)
     kv_gbs = b["kv"] / (ms_step * 1e-3) / 1e9
     tokens_s = w.bs * w.q_len / (ms_step * 1e-3)
     achieved = b["total"] / (dec_ms * 1e-3) / 1e9
+    flops = _algorithmic_flops(w)
+    tflops = flops / (dec_ms * 1e-3) / 1e12
     line = {
         "metric": "MLA decode KV-read GB/s (% of HBM peak; tokens/s) at B=64, 128 heads, "
                   "4k-average context",
@@ -407,6 +444,12 @@ def main() -> int:
         "ms_decode_merge": round(ms_dm, 5),
         "kv_read_gbs_decode_merge": round(b["kv"] / (ms_dm * 1e-3) / 1e9, 2),
         "ms_table_and_plan": round(ms_tp, 5),
+        "measured_copy_gbs": round(copy_gbs, 1),
+        "decode_pct_of_measured_copy": round(100.0 * achieved / copy_gbs, 2),
+        "mfma": {"algorithmic_tflop": round(flops / 1e12, 4),
+                 "achieved_tflops": round(tflops, 2), "peak_tflops": MFMA_PEAK_TFLOPS,
+                 "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
+                 "note": "dense bf16 MFMA peak (the fp8 cache is converted to bf16 in LDS)"},
         "append": append,
         "step_launch": "hip graph replay" if a.graph else "eager",
         "ms_per_step_eager": None if ms_step_eager is None else round(ms_step_eager, 5),
