@@ -11,6 +11,8 @@
 // request.  One work-group does everything: prefix sums over requests, a
 // binary search per cut for its cost position, and per-cut bookkeeping for the
 // rest.  Deterministic.
+#include <atomic>
+
 #include "block_table.h"
 
 namespace mla {
@@ -450,14 +452,20 @@ inline size_t plan_lds(int bs, int parts) {
                                                        : plan_lds_ints(bs, parts);
 }
 
-// Raises the dynamic-LDS limit of a planning kernel once.
+// Raises the dynamic-LDS limit of a planning kernel once per device (the
+// attribute is set for the current device).  `done` holds one flag per device
+// ordinal; calls from several host threads may both set it, which is harmless.
+constexpr int kMaxDevices = 64;
 template <typename K>
-mla_status allow_plan_lds(K kernel, bool& done, const char* who) {
-  if (!done) {
+mla_status allow_plan_lds(K kernel, std::atomic<bool> (&done)[kMaxDevices], const char* who) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess)
+    return fail(MLA_ERR_DEVICE, std::string(who) + ": no current device");
+  if (dev < 0 || dev >= kMaxDevices || !done[dev].load(std::memory_order_acquire)) {
     if (hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                             160 * 1024) != hipSuccess)
       return fail(MLA_ERR_DEVICE, std::string(who) + ": cannot raise the LDS limit");
-    done = true;
+    if (dev >= 0 && dev < kMaxDevices) done[dev].store(true, std::memory_order_release);
   }
   return MLA_OK;
 }
@@ -473,7 +481,7 @@ extern "C" mla_status mla_plan_splits(const int32_t* seq_lens, int32_t bs, int32
   if (st != MLA_OK) return st;
   const int overhead = plan_overhead_q(rows_per_req);
   const size_t lds = sizeof(int) * plan_lds(bs, num_parts);
-  static bool lds_raised = false;
+  static std::atomic<bool> lds_raised[kMaxDevices];
   const mla_status la = allow_plan_lds(plan_splits_kernel, lds_raised, "mla_plan_splits");
   if (la != MLA_OK) return la;
   hipLaunchKernelGGL(plan_splits_kernel, dim3(1), dim3(kPlanThreads), lds, stream, seq_lens, bs,
@@ -500,7 +508,7 @@ extern "C" mla_status mla_build_table_and_plan(
   const int64_t blocks = 1 + (int64_t)bs * per_row;
   if (blocks > 0x7fffffff) return fail(MLA_ERR_UNSUPPORTED, std::string(who) + ": table too large");
   const size_t lds = sizeof(int) * plan_lds(bs, num_parts);
-  static bool lds_raised = false;
+  static std::atomic<bool> lds_raised[kMaxDevices];
   st = allow_plan_lds(table_and_plan_kernel, lds_raised, who);
   if (st != MLA_OK) return st;
   hipLaunchKernelGGL(table_and_plan_kernel, dim3((unsigned)blocks), dim3(kPlanThreads), lds,
