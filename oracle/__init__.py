@@ -21,7 +21,8 @@ from .paged_mla import (  # noqa: F401
     request_keys,
     attend,
     paged_decode,
+    paged_decode_q8,
     merge_states,
 )
-from .kv_append import e4m3fn_encode, quantize_rows, set_kv_buffer  # noqa: F401
+from .kv_append import e4m3fn_encode, quantize_rows, quantize_q, set_kv_buffer  # noqa: F401
 from .plan import plan_reference, check_plan, plan_overhead, plan_fixed, check_fixed_plan  # noqa: F401

@@ -85,3 +85,11 @@ def set_kv_buffer(kv: np.ndarray, slots: np.ndarray, k_bits: np.ndarray, kv_dtyp
         else:
             raise ValueError(kv_dtype)
     return out
+
+
+def quantize_q(q_bits: np.ndarray, q_scale: float) -> np.ndarray:
+    """The fp8 branch of the FlashMLA page's forward_decode quantises the
+    query with the cache's scale before attention (scaled_fp8_quant with
+    q_scale = k_scale): code = e4m3fn(q / q_scale), the same rounding and
+    saturation as the cache bytes.  Returns uint8 codes of q's shape."""
+    return quantize_rows(q_bits, q_scale)

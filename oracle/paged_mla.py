@@ -145,6 +145,31 @@ def paged_decode(q_bits, kv, kv_dtype, kv_descale, req_to_token, req_pool_indice
     return o.reshape(bs, n, H, V_DIM), lse.reshape(bs, n, H)
 
 
+def paged_decode_q8(q_codes, q_descale, kv, kv_dtype, kv_descale, req_to_token,
+                    req_pool_indices, seq_lens, softmax_scale, causal=True, rows=None):
+    """paged_decode with an fp8 query (the fp8 branch of the FlashMLA page's
+    forward_decode: q quantised to e4m3fn with the cache scale, then
+    descale_q applied to the scores): the query row's value is
+    e4m3fn(code) * q_descale.  q_codes: uint8 [bs, q_len, H, 576]."""
+    bs, n, H, D = q_codes.shape
+    assert D == LATENT_DIM
+    width = max(1, -(-int(np.max(seq_lens)) // PAGE_SIZE)) if bs else 1
+    bt = block_table(req_to_token, req_pool_indices, seq_lens, width)
+    o = np.full((bs, n * H, V_DIM), np.nan)
+    lse = np.full((bs, n * H), np.nan)
+    for b in range(bs):
+        sel = np.arange(n * H) if rows is None else np.asarray(rows.get(b, []), dtype=np.int64)
+        if sel.size == 0:
+            continue
+        L = int(seq_lens[b])
+        K = request_keys(kv, kv_dtype, kv_descale, bt[b], L)
+        Q = e4m3fn_to_f64(q_codes[b].reshape(n * H, D)[sel]) * float(q_descale)
+        i = sel // H
+        last = (L - n + i) if causal else np.full(sel.size, L - 1)
+        o[b, sel], lse[b, sel] = attend(Q, K, softmax_scale, last)
+    return o.reshape(bs, n, H, V_DIM), lse.reshape(bs, n, H)
+
+
 def merge_states(o_parts: np.ndarray, lse_parts: np.ndarray, indptr: np.ndarray):
     """Exact merge of partial attention states over disjoint key sets.
 

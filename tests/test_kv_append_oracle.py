@@ -125,3 +125,58 @@ def test_set_kv_buffer_fp8_error_bound_and_decode_sees_new_rows():
     bt = oracle.block_table(r2t, np.array([0]), np.array([L]), 3)
     K = oracle.request_keys(out2, "fp8_e4m3", scale, bt[0], L)
     assert np.array_equal(K[L - 1], oracle.e4m3fn_to_f64(oracle.quantize_rows(row_bits[0], scale)) * scale)
+
+
+# ------------------------------------------------------------ fp8 query
+
+def test_quantize_q_shape_and_codes():
+    rng = np.random.default_rng(21)
+    q = (rng.standard_normal((2, 1, 4, 576)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    c = oracle.quantize_q(q, 0.02)
+    assert c.shape == q.shape and c.dtype == np.uint8
+    assert np.array_equal(c.reshape(-1), oracle.quantize_rows(q.reshape(-1), 0.02))
+
+
+def _tiny_q8_case():
+    from workloads import make_custom
+    w = make_custom("q8", bs=2, heads=4, q_len=2, seq_lens=[70, 5], seed=23, value_scale=0.5)
+    rng = np.random.default_rng(24)
+    codes = rng.integers(0, 0x7E, size=w.q_bits.shape).astype(np.uint8)
+    codes |= (rng.random(w.q_bits.shape) < 0.5).astype(np.uint8) << 7     # random signs
+    return w, codes
+
+
+def test_decode_q8_equals_decode_of_the_dequantised_query():
+    """With a power-of-two q scale, code * scale is exact in bf16: the fp8-query
+    decode must equal the bf16 decode of those values."""
+    w, codes = _tiny_q8_case()
+    dq = 2.0 ** -5
+    vals = oracle.e4m3fn_to_f64(codes) * dq
+    q_bits = (vals.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(oracle.bf16_to_f64(q_bits), vals)             # exact in bf16
+    args = (w.kv, w.kv_dtype, w.kv_descale, w.req_to_token, w.req_pool_indices, w.seq_lens,
+            w.softmax_scale, w.causal)
+    o8, l8 = oracle.paged_decode_q8(codes, dq, *args)
+    o, l = oracle.paged_decode(q_bits, *args)
+    assert np.allclose(o8, o, rtol=0, atol=1e-12) and np.allclose(l8, l, rtol=0, atol=1e-12)
+    # and quantising those values gives the codes back
+    assert np.array_equal(oracle.quantize_q(q_bits, dq), codes)
+
+
+def test_decode_q8_descale_scales_the_scores_only():
+    """q_descale multiplies every score: it is the same as folding it into the
+    softmax scale, and the output stays a weighted mean of the value rows."""
+    w, codes = _tiny_q8_case()
+    base = (w.kv, w.kv_dtype, w.kv_descale, w.req_to_token, w.req_pool_indices, w.seq_lens)
+    o_a, l_a = oracle.paged_decode_q8(codes, 0.37, *base, w.softmax_scale, w.causal)
+    o_b, l_b = oracle.paged_decode_q8(codes, 1.0, *base, w.softmax_scale * 0.37, w.causal)
+    assert np.allclose(o_a, o_b, rtol=0, atol=1e-12) and np.allclose(l_a, l_b, rtol=0, atol=1e-12)
+    # a zero scale leaves the plain mean of the visible value rows (lse = ln count)
+    o_0, l_0 = oracle.paged_decode_q8(codes, 0.0, *base, w.softmax_scale, w.causal)
+    L0 = int(w.seq_lens[1])
+    K = oracle.request_keys(w.kv, w.kv_dtype, w.kv_descale,
+                            oracle.block_table(w.req_to_token, w.req_pool_indices, w.seq_lens,
+                                               w.bt_width)[1], L0)
+    # request 1, token 0 of q_len 2 (causal) sees keys 0 .. L - 2
+    assert np.allclose(o_0[1, 0], K[:L0 - 1, :512].mean(axis=0), atol=1e-12)
+    assert np.allclose(l_0[1, 0], np.log(L0 - 1), atol=1e-12)
