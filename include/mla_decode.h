@@ -327,6 +327,31 @@ mla_status mla_set_kv_buffer(const void* k, int64_t k_row_stride, const int64_t*
                              int32_t num_tokens, void* kv_cache, int32_t kv_dtype,
                              int64_t num_pages, const float* kv_scale, hipStream_t stream);
 
+/*
+ * mla_quantize_q_fp8 — quantise query rows to e4m3fn with a per-tensor scale
+ * (the fp8 branch of forward_decode on the FlashMLA page runs
+ * scaled_fp8_quant(q, q_scale) with q_scale = the cache's k_scale before the
+ * attention call, and passes descale_q = k_scale).
+ *
+ * For every row i < num_rows and column c < 576:
+ *     q_fp8[i * 576 + c] = e4m3fn(q[i * q_row_stride + c] / *q_scale)
+ * with the quotient rounded to fp32, then to the nearest e4m3fn value (ties
+ * to even), magnitudes above 448 saturating to 448 and NaN to 0x7F/0xFF: the
+ * rounding of mla_set_kv_buffer's fp8 bytes.
+ *
+ *   q             bf16 rows of 576 (e.g. [bs, q_len, H, 576] seen as rows),
+ *                 16-byte aligned
+ *   q_row_stride  elements between rows, >= 576 and a multiple of 8
+ *   q_scale       device fp32 scalar, expected positive and finite
+ *   q_fp8         uint8 [num_rows, 576], contiguous, 8-byte aligned
+ *
+ * num_rows == 0 launches nothing (q may then be NULL).  Errors:
+ * INVALID_ARGUMENT for null pointers, num_rows < 0 or q_row_stride < 576;
+ * UNSUPPORTED for misaligned pointers or stride, or num_rows >= 2^31.
+ */
+mla_status mla_quantize_q_fp8(const void* q, int64_t q_row_stride, int64_t num_rows,
+                              const float* q_scale, void* q_fp8, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

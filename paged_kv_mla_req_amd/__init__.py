@@ -301,3 +301,23 @@ def set_kv_buffer(kv_cache: torch.Tensor, out_cache_loc: torch.Tensor, k: torch.
     _lib.check(_lib.lib().mla_set_kv_buffer(
         _p(k), k.stride(0) if k.shape[0] > 1 else LATENT_DIM, _p(out_cache_loc), k.shape[0],
         _p(kv_cache), code, kv_cache.shape[0], _p(kv_scale), _stream(stream)))
+
+
+def quantize_q_fp8(q: torch.Tensor, q_scale: torch.Tensor, out: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    """e4m3fn codes (uint8, q's shape) of q / q_scale (mla_quantize_q_fp8): the
+    query quantisation of the fp8 branch.  q: bf16 [..., 576], contiguous;
+    q_scale: device fp32 scalar."""
+    _need(q, "q", (torch.bfloat16,))
+    if q.shape[-1] != LATENT_DIM:
+        raise ValueError("q rows must be 576 wide")
+    _need(q_scale, "q_scale", (torch.float32,))
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.uint8, device=q.device)
+    _need(out, "out", (torch.uint8, torch.float8_e4m3fn))
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    rows = q.numel() // LATENT_DIM
+    _lib.check(_lib.lib().mla_quantize_q_fp8(_p(q), LATENT_DIM, rows, _p(q_scale), _p(out),
+                                             _stream(stream)))
+    return out

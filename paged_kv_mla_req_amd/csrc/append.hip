@@ -10,6 +10,11 @@
 // k / scale (ties to even, saturating at 448), the quotient rounded to fp32;
 // the decode multiplies the byte's value by the same per-tensor scale.
 //
+// The same kernel, with row i stored to row i, quantises the query for the
+// cache's fp8 branch (scaled_fp8_quant(q, q_scale) with q_scale = k_scale in
+// forward_decode): code = e4m3fn(q / q_scale), rounded and saturated as the
+// cache bytes are.
+//
 // How (gfx950): the work is pure data movement, bound by HBM (large appends)
 // or launch latency (one token per request).  One thread moves one 16-byte
 // chunk of 8 bf16 values; the 72 chunks of a row are consecutive threads, so
@@ -48,7 +53,7 @@ __global__ __launch_bounds__(kAppendThreads) void set_kv_kernel(
   const int64_t row = g / kAppendChunks;
   const int c = (int)(g - row * kAppendChunks);
   if (row >= n) return;
-  const int64_t s = slots[row];
+  const int64_t s = slots ? slots[row] : row;   // no slot list: row i goes to row i
   if (s < 0 || s >= num_slots) return;   // a slot outside the pool is never written
   const uint4 v = *reinterpret_cast<const uint4*>(k + row * k_row_stride + c * 8);
   if constexpr (!kFp8) {
@@ -106,4 +111,28 @@ extern "C" mla_status mla_set_kv_buffer(const void* k, int64_t k_row_stride,
     set_kv_kernel<false><<<blocks, kAppendThreads, 0, stream>>>(kk, k_row_stride, out_cache_loc,
                                                                 num_tokens, dst, num_slots, nullptr);
   return check_launch("mla_set_kv_buffer");
+}
+
+extern "C" mla_status mla_quantize_q_fp8(const void* q, int64_t q_row_stride, int64_t num_rows,
+                                         const float* q_scale, void* q_fp8, hipStream_t stream) {
+  using namespace mla;
+  if (!q_scale || !q_fp8 || (num_rows > 0 && !q))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "mla_quantize_q_fp8: null pointer");
+  if (num_rows < 0 || q_row_stride < kD)
+    return fail(MLA_ERR_INVALID_ARGUMENT,
+                "mla_quantize_q_fp8: need num_rows >= 0 and q_row_stride >= 576");
+  if ((reinterpret_cast<uintptr_t>(q) & 15u) || (q_row_stride & 7) ||
+      (reinterpret_cast<uintptr_t>(q_fp8) & 7u))
+    return fail(MLA_ERR_UNSUPPORTED,
+                "mla_quantize_q_fp8: q must be 16-byte aligned, q_row_stride a multiple of 8, "
+                "q_fp8 8-byte aligned");
+  if (num_rows > INT32_MAX)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_quantize_q_fp8: more than 2^31 - 1 rows");
+  if (num_rows == 0) return ok();
+  const int64_t threads = num_rows * kAppendChunks;
+  const unsigned blocks = (unsigned)((threads + kAppendThreads - 1) / kAppendThreads);
+  set_kv_kernel<true><<<blocks, kAppendThreads, 0, stream>>>(
+      static_cast<const uint16_t*>(q), q_row_stride, nullptr, (int32_t)num_rows,
+      static_cast<uint8_t*>(q_fp8), num_rows, q_scale);
+  return check_launch("mla_quantize_q_fp8");
 }

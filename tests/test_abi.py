@@ -169,3 +169,17 @@ def test_fixed_plan_argument_errors_and_bound():
     assert b(2, 4097, 32) == 6 and b(64, 8192, 32) == 256 and b(3, 0, 32) == 0
     assert b(1, 1, 1) == 1 and b(-1, 5, 32) == -1 and b(2, 5, 0) == -1
     assert b(16384, 2**31 - 1, 1) == 2**31 - 1
+
+
+def test_quantize_q_argument_errors():
+    f = _lib.lib().mla_quantize_q_fp8
+    assert f(None, 576, 4, FAKE, FAKE, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert f(FAKE, 576, 4, None, FAKE, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert f(FAKE, 576, 4, FAKE, None, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert f(FAKE, 576, -1, FAKE, FAKE, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert f(FAKE, 500, 4, FAKE, FAKE, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert f(FAKE, 580, 4, FAKE, FAKE, None) == _lib.MLA_ERR_UNSUPPORTED
+    assert f(P(0x1008), 576, 4, FAKE, FAKE, None) == _lib.MLA_ERR_UNSUPPORTED
+    assert f(FAKE, 576, 2**31, FAKE, FAKE, None) == _lib.MLA_ERR_UNSUPPORTED
+    assert _lib.lib().mla_last_error_message().startswith(b"mla_quantize_q_fp8")
+    assert f(None, 576, 0, FAKE, FAKE, None) == _lib.MLA_OK

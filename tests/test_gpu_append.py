@@ -169,3 +169,30 @@ def test_append_full_size_step(mla, name):
     assert torch.equal(flat[mask].view(torch.uint8) if fp8 else flat[mask].view(torch.int16),
                        before.view(pages * 64, 576)[mask].view(torch.uint8) if fp8
                        else before.view(pages * 64, 576)[mask].view(torch.int16))
+
+
+# ------------------------------------------------------------ query quantisation
+
+@pytest.mark.parametrize("name,scale", [("tiny", 1.0), ("fp8", 4.5 / 448), ("verify", 0.0125),
+                                        ("dsv3", 2.0 ** -6)])
+def test_quantize_q_fp8_bit_exact(mla, name, scale):
+    """The fp8 branch's query quantisation at the workloads' query shapes."""
+    w = make_workload(name)
+    d = to_device(w)
+    sc = torch.tensor([scale], dtype=torch.float32, device="cuda")
+    codes = mla.quantize_q_fp8(d.q, sc)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes.cpu().numpy(), oracle.quantize_q(w.q_bits, scale))
+
+
+def test_quantize_q_fp8_rounding_cases(mla):
+    v = oracle.e4m3fn_to_f64(np.arange(0x7F, dtype=np.uint8))
+    vals = np.concatenate([(v[:-1] + v[1:]) / 2, -(v[:-1] + v[1:]) / 2, v, -v,
+                           [500.0, -1e4, 2.0 ** -12, 0.0, -0.0]])
+    bits = (vals.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    q = np.resize(bits, (3, 576))
+    for scale in (1.0, 3.0):
+        sc = torch.tensor([scale], dtype=torch.float32, device="cuda")
+        codes = mla.quantize_q_fp8(_dev_u16(q), sc)
+        torch.cuda.synchronize()
+        assert np.array_equal(codes.cpu().numpy(), oracle.quantize_q(q, scale))
