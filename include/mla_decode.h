@@ -132,7 +132,8 @@ mla_status mla_build_block_table(const int32_t* req_to_token, int32_t r2t_rows,
  *                 the page's is_fp8_kvcache flag; the rule does not use it).
  *
  * Errors: INVALID_ARGUMENT for null pointers, bs <= 0, num_parts <= 0 or a bad
- * dtype; UNSUPPORTED for rows_per_req outside 1..512; CAPACITY for
+ * dtype; UNSUPPORTED for rows_per_req outside 1..512 or a tile_plan that is
+ * not 16-byte aligned (rows are written 16 bytes at a time); CAPACITY for
  * bs > MLA_MAX_BATCH, num_parts > MLA_MAX_PARTS or num_parts above the current
  * device's CU count (the page asserts num_sm_parts <= preallocated count).
  */
@@ -169,7 +170,7 @@ mla_status mla_plan_splits(const int32_t* seq_lens, int32_t bs, int32_t rows_per
  * decode and merge then write o = 0 and lse = -inf for every row.
  *
  * Errors: INVALID_ARGUMENT for null pointers or bs, tile_pages or max_parts
- * <= 0; CAPACITY for bs > MLA_MAX_BATCH, max_parts > MLA_MAX_DECODE_PARTS,
+ * <= 0; UNSUPPORTED for a tile_plan that is not 16-byte aligned; CAPACITY for bs > MLA_MAX_BATCH, max_parts > MLA_MAX_DECODE_PARTS,
  * or when the hint allows more pieces than max_parts
  * (mla_fixed_split_parts_bound(bs, hint, tile_pages) > max_parts).
  */

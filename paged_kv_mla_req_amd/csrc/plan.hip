@@ -435,6 +435,8 @@ mla_status check_plan_args(const char* who, const int32_t* seq_lens, int32_t bs,
     return fail(MLA_ERR_INVALID_ARGUMENT, w + ": unknown kv_dtype");
   if (rows_per_req < 1 || rows_per_req > MLA_MAX_ROWS_PER_REQ)
     return fail(MLA_ERR_UNSUPPORTED, w + ": rows_per_req must be in 1..512");
+  if (reinterpret_cast<uintptr_t>(tile_plan) & 15u)
+    return fail(MLA_ERR_UNSUPPORTED, w + ": tile_plan must be 16-byte aligned");
   if (bs > MLA_MAX_BATCH)
     return fail(MLA_ERR_CAPACITY, w + ": bs above " + std::to_string(MLA_MAX_BATCH));
   if (num_parts > MLA_MAX_PARTS)
@@ -608,6 +610,8 @@ extern "C" mla_status mla_plan_fixed_splits(const int32_t* seq_lens, int32_t bs,
     return fail(MLA_ERR_CAPACITY, w + ": bs above " + std::to_string(MLA_MAX_BATCH));
   if (max_parts > MLA_MAX_DECODE_PARTS)
     return fail(MLA_ERR_CAPACITY, w + ": max_parts above " + std::to_string(MLA_MAX_DECODE_PARTS));
+  if (reinterpret_cast<uintptr_t>(tile_plan) & 15u)
+    return fail(MLA_ERR_UNSUPPORTED, w + ": tile_plan must be 16-byte aligned");
   if (max_seq_len_hint >= 0 && fixed_parts_bound(bs, max_seq_len_hint, tile_pages) > max_parts)
     return fail(MLA_ERR_CAPACITY, w + ": " + std::to_string(bs) + " requests of up to " +
                                       std::to_string(max_seq_len_hint) +

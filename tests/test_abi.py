@@ -96,6 +96,7 @@ def test_plan_and_merge_argument_errors():
     assert g(FAKE, 2, 600, 4, 0, FAKE, FAKE, None) == _lib.MLA_ERR_UNSUPPORTED
     assert g(FAKE, 20000, 16, 4, 0, FAKE, FAKE, None) == _lib.MLA_ERR_CAPACITY
     assert g(FAKE, 2, 16, 600, 0, FAKE, FAKE, None) == _lib.MLA_ERR_CAPACITY
+    assert g(FAKE, 2, 16, 4, 0, P(0x1004), FAKE, None) == _lib.MLA_ERR_UNSUPPORTED
     m = lib.mla_merge_states
     assert m(None, FAKE, FAKE, 2, 16, FAKE, None, None) == _lib.MLA_ERR_INVALID_ARGUMENT
     assert m(FAKE, FAKE, FAKE, 0, 16, FAKE, None, None) == _lib.MLA_ERR_INVALID_ARGUMENT
@@ -162,6 +163,7 @@ def test_fixed_plan_argument_errors_and_bound():
     assert f(FAKE, 2, 32, 0, -1, FAKE, FAKE, None) == _lib.MLA_ERR_INVALID_ARGUMENT
     assert f(FAKE, 20000, 32, 8, -1, FAKE, FAKE, None) == _lib.MLA_ERR_CAPACITY
     assert f(FAKE, 2, 32, 65537, -1, FAKE, FAKE, None) == _lib.MLA_ERR_CAPACITY
+    assert f(FAKE, 2, 32, 8, -1, P(0x1004), FAKE, None) == _lib.MLA_ERR_UNSUPPORTED
     # 2 requests of up to 4097 tokens = 65 pages = 3 tiles of 32 pages each: 6 > 5
     assert f(FAKE, 2, 32, 5, 4097, FAKE, FAKE, None) == _lib.MLA_ERR_CAPACITY
     assert lib.mla_last_error_message().startswith(b"mla_plan_fixed_splits")
