@@ -196,3 +196,35 @@ def test_quantize_q_fp8_rounding_cases(mla):
         codes = mla.quantize_q_fp8(_dev_u16(q), sc)
         torch.cuda.synchronize()
         assert np.array_equal(codes.cpu().numpy(), oracle.quantize_q(q, scale))
+
+
+def test_quantized_query_decodes_as_the_fp8_query_oracle(mla):
+    """The fp8 branch end to end on small shapes: the query quantised on the GPU
+    (mla_quantize_q_fp8) and, with a power-of-two scale, taken back to bf16
+    exactly (code value * scale, a test-side step), then decoded on the GPU over
+    an fp8 cache, matches the oracle's fp8-query decode of the GPU's codes."""
+    from tests.test_gpu_parity import _np, assert_close, run
+    from workloads import make_custom
+
+    w = make_custom("q8dec", bs=3, heads=16, q_len=1, seq_lens=[37, 300, 1100], seed=61,
+                    kv_dtype="fp8_e4m3", value_scale=0.5)
+    d = to_device(w)
+    dq = 2.0 ** -4
+    sc = torch.tensor([dq], dtype=torch.float32, device="cuda")
+    codes = mla.quantize_q_fp8(d.q, sc)
+    torch.cuda.synchronize()
+    c_np = codes.cpu().numpy()
+    assert np.array_equal(c_np, oracle.quantize_q(w.q_bits, dq))
+    q_deq = (codes.view(torch.float8_e4m3fn).to(torch.float32) * dq).to(torch.bfloat16)
+    vals = oracle.e4m3fn_to_f64(c_np) * dq
+    assert np.array_equal(q_deq.float().cpu().numpy().astype(np.float64), vals)   # exact
+    bt = mla.build_block_table(d.req_to_token, d.req_pool_indices, d.seq_lens, w.bt_width)
+    plan = mla.plan_splits(d.seq_lens, w.rows_per_req, 5, w.kv_dtype)
+    out, lse = mla.decode(q_deq.contiguous(), d.kv, bt, d.seq_lens, w.softmax_scale,
+                          kv_dtype=w.kv_dtype, kv_descale=d.kv_descale, causal=w.causal,
+                          plan=plan)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.paged_decode_q8(c_np, dq, w.kv, w.kv_dtype, w.kv_descale,
+                                            w.req_to_token, w.req_pool_indices, w.seq_lens,
+                                            w.softmax_scale, w.causal)
+    assert_close(_np(out), _np(lse), o_ref, lse_ref)
