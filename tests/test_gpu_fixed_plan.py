@@ -184,3 +184,19 @@ def test_captured_append_and_fixed_plan_step_replays(mla):
     o_ref, lse_ref = oracle.paged_decode(w.q_bits, kv_ref, "bf16", 1.0, w.req_to_token,
                                          w.req_pool_indices, w.seq_lens, w.softmax_scale, w.causal)
     assert_close(_np(out), _np(lse), o_ref, lse_ref)
+
+
+def test_fixed_plan_decode_with_empty_and_one_token_requests(mla):
+    """Empty requests (no piece: the merge writes o = 0, lse = -inf), a
+    one-token request, and requests ending exactly on a tile boundary."""
+    lens = [0, 1, 256, 0, 257, 64]
+    w = make_custom("fixed_edge", bs=len(lens), heads=16, q_len=1, seq_lens=lens, seed=44,
+                    value_scale=0.5)
+    d = to_device(w)
+    T = 4                                      # 256 tokens = exactly one tile
+    out, lse = _fixed_decode(mla, d, w, w.bt_width, T, _need(lens, T) + 1)
+    o, l = _np(out), _np(lse)
+    o_ref, lse_ref = ref(w)
+    assert_close(o, l, o_ref, lse_ref)
+    for b in (0, 3):
+        assert np.all(o[b] == 0) and np.all(l[b] == -np.inf)
