@@ -117,6 +117,20 @@ def measured_copy_gbs(torch, mib: int = 2048, reps: int = 10) -> float:
     return 2 * (mib << 20) / (ms * 1e-3) / 1e9
 
 
+def _kernel_of(kv_dtype: str):
+    """(source file under csrc/, kernel name) of the decode kernel that runs
+    for a cache dtype."""
+    if kv_dtype == "bf16":
+        return "decode_tile.hip", "mla_decode_tile_kernel"
+    return "decode.hip", "mla_decode_kernel<true>"
+
+
+def _kernel_src(root: str, workload: str) -> str:
+    from workloads import CONFIGS
+    return os.path.join(root, "paged_kv_mla_req_amd", "csrc",
+                        _kernel_of(CONFIGS[workload]["kv_dtype"])[0])
+
+
 def _traffic_path(root: str, workload: str) -> str:
     from workloads import CONFIGS
     tag = "bf16" if CONFIGS[workload]["kv_dtype"] == "bf16" else "fp8"
@@ -141,7 +155,8 @@ def _traffic(root: str, kernel_src: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def traffic_from_counters(fetch_csv: str, write_csv: str, calib_mib: int, root: str) -> dict:
+def traffic_from_counters(fetch_csv: str, write_csv: str, calib_mib: int, root: str,
+                          workload: str) -> dict:
     """HBM bytes per decode launch from FETCH_SIZE and WRITE_SIZE (KiB per
     dispatch), each scaled by calib_mib MiB over what the same counter read
     for the calibration kernel (bitwise not over calib_mib MiB)."""
@@ -155,7 +170,7 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, calib_mib: int, root: 
                 if r["Counter_Name"] != counter:
                     continue
                 v = float(r["Counter_Value"]) * 1024.0
-                if "mla_decode_kernel" in r["Kernel_Name"]:
+                if "mla_decode" in r["Kernel_Name"] and "kernel" in r["Kernel_Name"]:
                     dec.append(v)
                 elif "bitwise_not" in r["Kernel_Name"].lower():
                     cal.append(v)
@@ -166,7 +181,7 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, calib_mib: int, root: 
 
     fetch, f_fac, f_raw = read(fetch_csv, "FETCH_SIZE")
     write, w_fac, w_raw = read(write_csv, "WRITE_SIZE")
-    src = os.path.join(root, "paged_kv_mla_req_amd", "csrc", "decode.hip")
+    src = _kernel_src(root, workload)
     with open(src, "rb") as f:
         sha = hashlib.sha256(f.read()).hexdigest()
     return {"hbm_bytes_per_launch": round(fetch + write), "fetch_bytes": round(fetch),
@@ -251,7 +266,7 @@ def main() -> int:
     if a.traffic_from:
         root = os.path.dirname(os.path.abspath(__file__))
         rec = traffic_from_counters(a.traffic_from[0], a.traffic_from[1],
-                                    a.calib_copy_mib or 256, root)
+                                    a.calib_copy_mib or 256, root, a.workload)
         rec["workload"] = a.workload
         path = _traffic_path(root, a.workload)
         with open(path, "w") as f:
@@ -464,10 +479,10 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": _traffic(os.path.dirname(os.path.abspath(__file__)),
-                                os.path.join(os.path.dirname(os.path.abspath(__file__)),
-                                             "paged_kv_mla_req_amd", "csrc", "decode.hip"),
+                                _kernel_src(os.path.dirname(os.path.abspath(__file__)),
+                                            a.workload),
                                 a.workload),
-            "kernel": "mla_decode_kernel<%s>" % ("true" if w.kv_dtype != "bf16" else "false"),
+            "kernel": _kernel_of(w.kv_dtype)[1],
             "bytes_per_launch": b["total"],
         },
     }

@@ -19,8 +19,11 @@
  *
  * Conventions shared by every entry point
  *   - Every pointer is device memory unless its comment says "host".
- *   - The caller owns every buffer.  The library allocates no device memory
- *     and keeps no state between calls apart from a thread-local error text.
+ *   - The caller owns every buffer.  The library allocates no device memory.
+ *     State kept between calls: per host thread, the last error text and the
+ *     events of mla_decode_time_next_launch (used by the next decode only);
+ *     per device, whether the planner kernels' LDS limit was raised (set
+ *     once, on their first launch there).
  *   - Calls are asynchronous on the given HIP stream (0 = the null stream),
  *     never synchronise and never read device memory on the host, so they can
  *     be captured in a HIP graph (the FlashMLA page prepares fixed-capacity
@@ -41,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 1
+#define MLA_ABI_VERSION 2
 #define MLA_PAGE_SIZE 64
 #define MLA_LATENT_DIM 576
 #define MLA_V_DIM 512
@@ -203,8 +206,13 @@ mla_status mla_build_table_and_plan(const int32_t* req_to_token, int32_t r2t_row
                                     hipStream_t stream);
 
 /* Host helpers: upper bound of split_indptr[bs] (= bs + num_parts), and the
- * bytes of the partial_o + partial_lse buffers that bound needs. */
+ * bytes of the decode workspace that bound needs: partial_o (bf16
+ * [slots, rows_per_req, 512]) plus partial_lse (fp32 [slots, rows_per_req])
+ * with slots = bs + num_parts (the page's backends take one preallocated
+ * workspace buffer).  mla_partial_bytes is the same function under its
+ * earlier name.  0 for negative sizes. */
 int32_t mla_max_total_splits(int32_t bs, int32_t num_parts);
+size_t mla_workspace_bytes(int32_t bs, int32_t rows_per_req, int32_t num_parts);
 size_t mla_partial_bytes(int32_t bs, int32_t rows_per_req, int32_t num_parts);
 
 /* Host helper: CU count of the current device (the default num_parts), or -1. */
@@ -223,8 +231,10 @@ int32_t mla_device_num_cus(void);
  *     o_r = sum_j exp(s_j - lse_r) V_j.
  * A piece computes these sums over its own pages.  A request with exactly
  * one piece is final: o goes to out (bf16, round to nearest even) and lse to
- * lse.  Otherwise each piece writes its (o, lse) in fp32 to partial slot
- * split_indptr[b] + piece, and mla_merge_states finishes the request.
+ * lse.  Otherwise each piece writes its o (normalised by its own row sum,
+ * rounded to bf16) and its lse (fp32) to partial slot split_indptr[b] + piece,
+ * and mla_merge_states finishes the request.  A slot outside
+ * [0, partial_slots) is not written.
  *
  *   q             bf16 [bs, q_len, num_heads, 576], contiguous
  *   kv_cache      [num_pages, 64, 576] bf16, or bytes for MLA_KV_FP8_E4M3
@@ -238,14 +248,17 @@ int32_t mla_device_num_cus(void);
  *                 one scale for K and V (the page's descale_k).  delta must be
  *                 finite; it may be 0 or negative.  Read on the device, so a
  *                 captured graph picks up a new value without re-capture.
- *   partial_o     fp32 [partial_slots, q_len*num_heads, 512]
+ *   partial_o     bf16 [partial_slots, q_len*num_heads, 512], 16-byte aligned
  *   partial_lse   fp32 [partial_slots, q_len*num_heads]
+ *   partial_slots slots of the workspace (the decode's capacity argument;
+ *                 the page's graph state preallocates fixed capacities)
  *   out           bf16 [bs, q_len, num_heads, 512] (rows of split requests
  *                 are written by mla_merge_states)
  *   lse           fp32 [bs, q_len, num_heads] natural-log LSE, or NULL
  *
- * Block-table entries outside [0, num_pages) are a caller error; the kernel
- * then reads page 0 instead, so it never leaves the pool.
+ * Block-table entries outside [0, num_pages), or a page index at or past
+ * bt_row_stride, are a caller error: such a page is never read, and its keys
+ * are masked (they contribute nothing), so the kernel never leaves the pool.
  *
  * Errors: INVALID_ARGUMENT for null pointers, non-positive sizes, a
  * negative or non-finite scale, or fp8 with a NULL kv_descale; UNSUPPORTED for
@@ -257,7 +270,7 @@ mla_status mla_decode(const void* q, int32_t bs, int32_t q_len, int32_t num_head
                       const int32_t* block_table, int32_t bt_row_stride,
                       const int32_t* seq_lens, const int32_t* tile_plan, int32_t num_parts,
                       const int32_t* split_indptr, float softmax_scale, int32_t causal,
-                      const float* kv_descale, float* partial_o, float* partial_lse,
+                      const float* kv_descale, void* partial_o, float* partial_lse,
                       int32_t partial_slots, void* out, float* lse, hipStream_t stream);
 
 /*
@@ -278,20 +291,27 @@ mla_status mla_decode_time_next_launch(hipEvent_t start, hipEvent_t stop);
  * For request b with k = split_indptr[b+1] - split_indptr[b] pieces and each
  * row r:  M = max_k lse_k,  LSE = M + ln sum_k exp(lse_k - M),
  *         o = sum_k exp(lse_k - LSE) * o_k.
- * Pieces with lse = -inf weigh 0; if all do, o = 0 and LSE = -inf.
+ * Pieces with lse = -inf weigh 0, and so does a piece whose slot
+ * split_indptr[b] + s lies outside [0, partial_slots) (it is not read); if all
+ * do, o = 0 and LSE = -inf.
  * k == 1: the request is skipped (mla_decode already wrote it).
  * k == 0: o = 0 and LSE = -inf are written.
  * A two-way merge of arbitrary states is the case split_indptr = {0, 2, 4, ...}.
  *
- *   partial_o     fp32 [slots, rows_per_req, 512];  partial_lse fp32 [slots, rows_per_req]
- *   out           bf16 [bs, rows_per_req, 512];     lse fp32 [bs, rows_per_req] or NULL
+ *   partial_o     bf16 [partial_slots, rows_per_req, dv], 16-byte aligned
+ *   partial_lse   fp32 [partial_slots, rows_per_req]
+ *   dv            value width; must be 512 (kv_lora_rank)
+ *   out           bf16 [bs, rows_per_req, dv], 16-byte aligned
+ *   lse           fp32 [bs, rows_per_req] or NULL
  *
- * Errors: INVALID_ARGUMENT for null pointers or bs <= 0; UNSUPPORTED for
- * rows_per_req outside 1..512.
+ * Errors: INVALID_ARGUMENT for null pointers, bs <= 0 or partial_slots < 0;
+ * UNSUPPORTED for rows_per_req outside 1..512, dv != 512 or misaligned
+ * partial_o / out.
  */
-mla_status mla_merge_states(const float* partial_o, const float* partial_lse,
-                            const int32_t* split_indptr, int32_t bs, int32_t rows_per_req,
-                            void* out, float* lse, hipStream_t stream);
+mla_status mla_merge_states(const void* partial_o, const float* partial_lse,
+                            int32_t partial_slots, const int32_t* split_indptr, int32_t bs,
+                            int32_t rows_per_req, int32_t dv, void* out, float* lse,
+                            hipStream_t stream);
 
 /*
  * mla_set_kv_buffer — store the new tokens' latent rows in the paged cache

@@ -46,6 +46,19 @@ def _need(t: torch.Tensor, name: str, dtypes, ndim: Optional[int] = None):
         raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
 
 
+def _same_device(*named):
+    """All given tensors (None skipped) on one device."""
+    devs = {(n, t.device) for n, t in named if t is not None}
+    if len({d for _, d in devs}) > 1:
+        raise ValueError("tensors on different devices: " +
+                         ", ".join(f"{n}={d}" for n, d in sorted(devs, key=str)))
+
+
+def _shape(t: torch.Tensor, name: str, shape) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {tuple(shape)}, got {tuple(t.shape)}")
+
+
 def _kv_code(kv_dtype) -> int:
     if isinstance(kv_dtype, int):
         return kv_dtype
@@ -67,6 +80,12 @@ def max_total_splits(bs: int, num_parts: int) -> int:
     return int(_lib.lib().mla_max_total_splits(bs, num_parts))
 
 
+def workspace_bytes(bs: int, rows_per_req: int, num_parts: int) -> int:
+    """Bytes of partial_o (bf16) + partial_lse (fp32) for bs + num_parts slots
+    (mla_workspace_bytes)."""
+    return int(_lib.lib().mla_workspace_bytes(bs, rows_per_req, num_parts))
+
+
 def build_block_table(req_to_token: torch.Tensor, req_pool_indices: torch.Tensor,
                       seq_lens: torch.Tensor, width: int, pad_value: int = -1,
                       max_seq_len_hint: int = -1, out: Optional[torch.Tensor] = None,
@@ -79,6 +98,11 @@ def build_block_table(req_to_token: torch.Tensor, req_pool_indices: torch.Tensor
     if out is None:
         out = torch.empty((bs, width), dtype=torch.int32, device=seq_lens.device)
     _need(out, "out", (torch.int32,), 2)
+    _shape(req_pool_indices, "req_pool_indices", (bs,))
+    if out.shape[0] < bs:
+        raise ValueError(f"out has {out.shape[0]} rows, needs {bs}")
+    _same_device(("req_to_token", req_to_token), ("req_pool_indices", req_pool_indices),
+                 ("seq_lens", seq_lens), ("out", out))
     _lib.check(_lib.lib().mla_build_block_table(
         _p(req_to_token), req_to_token.shape[0], req_to_token.stride(0), _p(req_pool_indices),
         _p(seq_lens), bs, PAGE_SIZE, _p(out), out.shape[1], pad_value, max_seq_len_hint,
@@ -102,8 +126,11 @@ def plan_splits(seq_lens: torch.Tensor, rows_per_req: int, num_parts: Optional[i
         split_indptr = torch.empty((bs + 1,), dtype=torch.int32, device=seq_lens.device)
     _need(tile_plan, "tile_plan", (torch.int32,), 2)
     _need(split_indptr, "split_indptr", (torch.int32,), 1)
-    if tile_plan.shape[0] < num_parts or split_indptr.shape[0] < bs + 1:
+    if tile_plan.shape[0] < num_parts or tile_plan.shape[1] != 8 or \
+            split_indptr.shape[0] < bs + 1:
         raise ValueError("plan buffers too small")
+    _same_device(("seq_lens", seq_lens), ("tile_plan", tile_plan),
+                 ("split_indptr", split_indptr))
     _lib.check(_lib.lib().mla_plan_splits(_p(seq_lens), bs, rows_per_req, num_parts,
                                           _kv_code(kv_dtype), _p(tile_plan), _p(split_indptr),
                                           _stream(stream)))
@@ -134,6 +161,8 @@ def plan_fixed_splits(seq_lens: torch.Tensor, tile_pages: int = 32,
     _need(split_indptr, "split_indptr", (torch.int32,), 1)
     if tile_plan.shape != (max_parts, 8) or split_indptr.shape != (bs + 1,):
         raise ValueError("tile_plan must be [max_parts, 8] and split_indptr [bs + 1]")
+    _same_device(("seq_lens", seq_lens), ("tile_plan", tile_plan),
+                 ("split_indptr", split_indptr))
     _lib.check(_lib.lib().mla_plan_fixed_splits(_p(seq_lens), bs, tile_pages, max_parts,
                                                 max_seq_len_hint, _p(tile_plan),
                                                 _p(split_indptr), _stream(stream)))
@@ -165,8 +194,15 @@ def build_table_and_plan(req_to_token: torch.Tensor, req_pool_indices: torch.Ten
     _need(out, "out", (torch.int32,), 2)
     _need(tile_plan, "tile_plan", (torch.int32,), 2)
     _need(split_indptr, "split_indptr", (torch.int32,), 1)
-    if tile_plan.shape[0] < num_parts or split_indptr.shape[0] < bs + 1:
+    if tile_plan.shape[0] < num_parts or tile_plan.shape[1] != 8 or \
+            split_indptr.shape[0] < bs + 1:
         raise ValueError("plan buffers too small")
+    _shape(req_pool_indices, "req_pool_indices", (bs,))
+    if out.shape[0] < bs:
+        raise ValueError(f"out has {out.shape[0]} rows, needs {bs}")
+    _same_device(("req_to_token", req_to_token), ("req_pool_indices", req_pool_indices),
+                 ("seq_lens", seq_lens), ("out", out), ("tile_plan", tile_plan),
+                 ("split_indptr", split_indptr))
     _lib.check(_lib.lib().mla_build_table_and_plan(
         _p(req_to_token), req_to_token.shape[0], req_to_token.stride(0), _p(req_pool_indices),
         _p(seq_lens), bs, PAGE_SIZE, _p(out), out.shape[1], pad_value, max_seq_len_hint,
@@ -177,10 +213,10 @@ def build_table_and_plan(req_to_token: torch.Tensor, req_pool_indices: torch.Ten
 
 def partial_buffers(bs: int, rows_per_req: int, num_parts: int,
                     device="cuda") -> Tuple[torch.Tensor, torch.Tensor]:
-    """Workspace for split pieces: partial o fp32 [bs+num_parts, R, 512] and
+    """Workspace for split pieces: partial o bf16 [bs+num_parts, R, 512] and
     partial lse fp32 [bs+num_parts, R]."""
     slots = max_total_splits(bs, num_parts)
-    return (torch.empty((slots, rows_per_req, V_DIM), dtype=torch.float32, device=device),
+    return (torch.empty((slots, rows_per_req, V_DIM), dtype=torch.bfloat16, device=device),
             torch.empty((slots, rows_per_req), dtype=torch.float32, device=device))
 
 
@@ -205,16 +241,31 @@ def mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tenso
     _need(seq_lens, "seq_lens", (torch.int32,), 1)
     _need(tile_plan, "tile_plan", (torch.int32,), 2)
     _need(split_indptr, "split_indptr", (torch.int32,), 1)
-    _need(partial_o, "partial_o", (torch.float32,), 3)
+    _need(partial_o, "partial_o", (torch.bfloat16,), 3)
     _need(partial_lse, "partial_lse", (torch.float32,), 2)
     _need(out, "out", (torch.bfloat16,), 4)
     if lse is not None:
         _need(lse, "lse", (torch.float32,), 3)
+        _shape(lse, "lse", (bs, q_len, heads))
     if kv_descale is not None:
         _need(kv_descale, "kv_descale", (torch.float32,))
+        if kv_descale.numel() < 1:
+            raise ValueError("kv_descale must hold one value")
     rows = q_len * heads
+    _shape(out, "out", (bs, q_len, heads, V_DIM))
     if partial_o.shape[1:] != (rows, V_DIM) or partial_lse.shape != (partial_o.shape[0], rows):
         raise ValueError("partial buffers do not match q")
+    if block_table.shape[0] < bs:
+        raise ValueError(f"block_table has {block_table.shape[0]} rows, needs {bs}")
+    _shape(seq_lens, "seq_lens", (bs,))
+    if split_indptr.shape[0] < bs + 1:
+        raise ValueError(f"split_indptr needs bs + 1 = {bs + 1} entries")
+    if tile_plan.shape[1] != 8:
+        raise ValueError("tile_plan must be [num_parts, 8]")
+    _same_device(("q", q), ("kv_cache", kv_cache), ("block_table", block_table),
+                 ("seq_lens", seq_lens), ("tile_plan", tile_plan), ("split_indptr", split_indptr),
+                 ("partial_o", partial_o), ("partial_lse", partial_lse), ("out", out),
+                 ("lse", lse), ("kv_descale", kv_descale))
     _lib.check(_lib.lib().mla_decode(
         _p(q), bs, q_len, heads, _p(kv_cache), code, kv_cache.shape[0], _p(block_table),
         block_table.shape[1], _p(seq_lens), _p(tile_plan), tile_plan.shape[0], _p(split_indptr),
@@ -232,21 +283,30 @@ def time_next_decode(start: torch.cuda.Event, stop: torch.cuda.Event) -> None:
 
 def merge_states(partial_o: torch.Tensor, partial_lse: torch.Tensor, split_indptr: torch.Tensor,
                  out: torch.Tensor, lse: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Exact LSE merge of split pieces into out (bf16) and lse (mla_merge_states)."""
-    _need(partial_o, "partial_o", (torch.float32,), 3)
+    """Exact LSE merge of split pieces into out (bf16) and lse (mla_merge_states).
+    partial_o: bf16 [slots, R, 512]; partial_lse: fp32 [slots, R]."""
+    _need(partial_o, "partial_o", (torch.bfloat16,), 3)
     _need(partial_lse, "partial_lse", (torch.float32,), 2)
     _need(split_indptr, "split_indptr", (torch.int32,), 1)
     _need(out, "out", (torch.bfloat16,))
     bs = split_indptr.shape[0] - 1
-    rows = partial_o.shape[1]
+    if bs < 1:
+        raise ValueError("split_indptr must have at least 2 entries")
+    slots, rows, dv = partial_o.shape
+    if dv != V_DIM:
+        raise ValueError("partial_o rows must be 512 wide")
+    _shape(partial_lse, "partial_lse", (slots, rows))
     if out.numel() != bs * rows * V_DIM:
         raise ValueError("out does not match split_indptr and partial_o")
     if lse is not None:
         _need(lse, "lse", (torch.float32,))
         if lse.numel() != bs * rows:
             raise ValueError("lse does not match")
-    _lib.check(_lib.lib().mla_merge_states(_p(partial_o), _p(partial_lse), _p(split_indptr), bs,
-                                           rows, _p(out), _p(lse), _stream(stream)))
+    _same_device(("partial_o", partial_o), ("partial_lse", partial_lse),
+                 ("split_indptr", split_indptr), ("out", out), ("lse", lse))
+    _lib.check(_lib.lib().mla_merge_states(_p(partial_o), _p(partial_lse), slots,
+                                           _p(split_indptr), bs, rows, V_DIM, _p(out), _p(lse),
+                                           _stream(stream)))
 
 
 def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,

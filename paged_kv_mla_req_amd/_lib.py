@@ -38,12 +38,14 @@ SIGNATURES = {
     "mla_plan_fixed_splits": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_p, _c_p]),
     "mla_fixed_split_parts_bound": (_c_i32, [_c_i32, _c_i32, _c_i32]),
     "mla_max_total_splits": (_c_i32, [_c_i32, _c_i32]),
+    "mla_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32]),
     "mla_partial_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32]),
     "mla_device_num_cus": (_c_i32, []),
     "mla_decode": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_p, _c_i32, _c_i64, _c_p, _c_i32,
                             _c_p, _c_p, _c_i32, _c_p, _c_f32, _c_i32, _c_p, _c_p, _c_p, _c_i32,
                             _c_p, _c_p, _c_p]),
-    "mla_merge_states": (_c_i32, [_c_p, _c_p, _c_p, _c_i32, _c_i32, _c_p, _c_p, _c_p]),
+    "mla_merge_states": (_c_i32, [_c_p, _c_p, _c_i32, _c_p, _c_i32, _c_i32, _c_i32, _c_p, _c_p,
+                                  _c_p]),
     "mla_decode_time_next_launch": (_c_i32, [_c_p, _c_p]),
     "mla_set_kv_buffer": (_c_i32, [_c_p, _c_i64, _c_p, _c_i32, _c_p, _c_i32, _c_i64, _c_p, _c_p]),
     "mla_quantize_q_fp8": (_c_i32, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),

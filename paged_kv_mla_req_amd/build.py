@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmla_decode.so")
-SOURCES = ["abi.hip", "block_table.hip", "plan.hip", "decode.hip", "merge.hip", "append.hip"]
+SOURCES = ["abi.hip", "block_table.hip", "plan.hip", "decode.hip", "decode_tile.hip", "merge.hip",
+           "append.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms stay disabled: the compiler would otherwise emit
@@ -30,11 +31,11 @@ COMMON_FLAGS = [
     "-Wno-unused-command-line-argument",
 ]
 
-# The decode kernel is compiled without NaN semantics, so that max() over
+# The decode kernels are compiled without NaN semantics, so that max() over
 # scores is a plain v_max/v_max3 (no operand canonicalisation).  No NaN
 # reaches it from the cache's unused slots: page tails are zero-filled, and
 # masked scores are -inf, scaled by a factor kept above 0.
-SOURCE_FLAGS = {"decode.hip": ["-fno-honor-nans"]}
+SOURCE_FLAGS = {"decode.hip": ["-fno-honor-nans"], "decode_tile.hip": ["-fno-honor-nans"]}
 
 
 def _hipcc() -> str:

@@ -52,10 +52,15 @@ int32_t mla_max_total_splits(int32_t bs, int32_t num_parts) {
   return bs + num_parts;
 }
 
-size_t mla_partial_bytes(int32_t bs, int32_t rows_per_req, int32_t num_parts) {
+size_t mla_workspace_bytes(int32_t bs, int32_t rows_per_req, int32_t num_parts) {
   if (bs < 0 || num_parts < 0 || rows_per_req < 0) return 0;
-  size_t slots = (size_t)bs + (size_t)num_parts;
-  return slots * (size_t)rows_per_req * (size_t)(MLA_V_DIM + 1) * sizeof(float);
+  const size_t slots = (size_t)bs + (size_t)num_parts;
+  // bf16 partial o [slots, rows, 512], then fp32 partial lse [slots, rows]
+  return slots * (size_t)rows_per_req * (MLA_V_DIM * sizeof(uint16_t) + sizeof(float));
+}
+
+size_t mla_partial_bytes(int32_t bs, int32_t rows_per_req, int32_t num_parts) {
+  return mla_workspace_bytes(bs, rows_per_req, num_parts);
 }
 
 int32_t mla_device_num_cus(void) {

@@ -54,6 +54,7 @@
 #include <hip/hip_ext.h>
 
 #include "common.h"
+#include "decode_tile.h"
 
 namespace mla {
 
@@ -885,7 +886,7 @@ __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_e
 mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
                   const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
                   const int32_t* __restrict__ tile_plan, const int32_t* __restrict__ split_indptr,
-                  const float* __restrict__ kv_descale, float* __restrict__ partial_o,
+                  const float* __restrict__ kv_descale, uint16_t* __restrict__ partial_o,
                   float* __restrict__ partial_lse, uint16_t* __restrict__ out,
                   float* __restrict__ lse_out, DecodeParams P) {
   // bf16: two compute buffers.  fp8: compute buffer 0, and two e4m3 staging
@@ -1292,13 +1293,13 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
       const bool to_partial = k > 1;
       const uint32_t ln = pinned_lane();
       const int r = row0 + (int)(ln & 31);
-      if (to_partial && slot < P.partial_slots) {
+      if (to_partial && slot >= 0 && slot < P.partial_slots) {
         if ((ln >> 5) == 0 && r < P.rows) partial_lse[slot * P.rows + r] = lse_val;
-        float* const po = partial_o + slot * P.rows * kDv;
+        uint16_t* const po = partial_o + slot * P.rows * kDv;
         if (row0 + kRowsPerWave <= P.rows)
-          store_rows<float, true>(oacc, inv, stage_all[wave], po, row0, P.rows, ln);
+          store_rows<uint16_t, true>(oacc, inv, stage_all[wave], po, row0, P.rows, ln);
         else
-          store_rows<float, false>(oacc, inv, stage_all[wave], po, row0, P.rows, ln);
+          store_rows<uint16_t, false>(oacc, inv, stage_all[wave], po, row0, P.rows, ln);
       } else if (!to_partial) {
         if (lse_out && (ln >> 5) == 0 && r < P.rows) lse_out[(int64_t)cb * P.rows + r] = lse_val;
         uint16_t* const ob = out + (int64_t)cb * P.rows * kDv;
@@ -1343,7 +1344,7 @@ extern "C" mla_status mla_decode(const void* q, int32_t bs, int32_t q_len, int32
                                  const int32_t* seq_lens, const int32_t* tile_plan,
                                  int32_t num_parts, const int32_t* split_indptr,
                                  float softmax_scale, int32_t causal, const float* kv_descale,
-                                 float* partial_o, float* partial_lse, int32_t partial_slots,
+                                 void* partial_o, float* partial_lse, int32_t partial_slots,
                                  void* out, float* lse, hipStream_t stream) {
   using namespace mla;
   const hipEvent_t ev_start = t_start_event, ev_stop = t_stop_event;
@@ -1379,12 +1380,27 @@ extern "C" mla_status mla_decode(const void* q, int32_t bs, int32_t q_len, int32
   p.rows = (int32_t)rows;
   p.causal = causal ? 1 : 0;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
+  if (kv_dtype == MLA_KV_BF16) {
+    TileParams pp;
+    pp.num_pages = num_pages;
+    pp.partial_slots = partial_slots;
+    pp.bt_stride = bt_row_stride;
+    pp.bs = bs;
+    pp.q_len = q_len;
+    pp.heads = num_heads;
+    pp.rows = (int32_t)rows;
+    pp.causal = causal ? 1 : 0;
+    pp.scale_log2 = softmax_scale * 1.4426950408889634f;
+    return launch_tile_decode(q, kv_cache, block_table, seq_lens, tile_plan, num_parts,
+                              split_indptr, partial_o, partial_lse, out, lse, pp, stream,
+                              ev_start, ev_stop);
+  }
   dim3 grid(num_parts, (unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
   auto launch = [&](auto kernel, const float* descale) {
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(q);
     const uint8_t* kvp = reinterpret_cast<const uint8_t*>(kv_cache);
     uint16_t* op = reinterpret_cast<uint16_t*>(out);
-    float* po = partial_o;
+    uint16_t* po = reinterpret_cast<uint16_t*>(partial_o);
     if (ev_start || ev_stop)
       hipExtLaunchKernelGGL(kernel, grid, dim3(kWaves * 64), 0, stream, ev_start, ev_stop, 0, qp,
                             kvp, block_table, seq_lens, tile_plan, split_indptr, descale,
@@ -1394,9 +1410,6 @@ extern "C" mla_status mla_decode(const void* q, int32_t bs, int32_t q_len, int32
                          seq_lens, tile_plan, split_indptr, descale, po, partial_lse, op,
                          lse, p);
   };
-  if (kv_dtype == MLA_KV_FP8_E4M3)
-    launch(mla_decode_kernel<true>, kv_descale);
-  else
-    launch(mla_decode_kernel<false>, nullptr);
+  launch(mla_decode_kernel<true>, kv_descale);
   return check_launch("mla_decode");
 }

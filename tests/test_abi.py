@@ -32,11 +32,14 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = _lib.lib()
-    assert lib.mla_abi_version() == 1
+    assert lib.mla_abi_version() == 2
     assert lib.mla_status_string(0) == b"ok"
     assert lib.mla_status_string(2) == b"unsupported"
     assert lib.mla_max_total_splits(64, 256) == 320
-    assert lib.mla_partial_bytes(64, 128, 256) == 320 * 128 * 513 * 4
+    # bf16 partial o (1024 bytes a row) and fp32 lse (4 bytes a row) per slot
+    assert lib.mla_workspace_bytes(64, 128, 256) == 320 * 128 * (512 * 2 + 4)
+    assert lib.mla_partial_bytes(64, 128, 256) == lib.mla_workspace_bytes(64, 128, 256)
+    assert lib.mla_workspace_bytes(-1, 128, 256) == 0
 
 
 P = ctypes.c_void_p
@@ -98,9 +101,14 @@ def test_plan_and_merge_argument_errors():
     assert g(FAKE, 2, 16, 600, 0, FAKE, FAKE, None) == _lib.MLA_ERR_CAPACITY
     assert g(FAKE, 2, 16, 4, 0, P(0x1004), FAKE, None) == _lib.MLA_ERR_UNSUPPORTED
     m = lib.mla_merge_states
-    assert m(None, FAKE, FAKE, 2, 16, FAKE, None, None) == _lib.MLA_ERR_INVALID_ARGUMENT
-    assert m(FAKE, FAKE, FAKE, 0, 16, FAKE, None, None) == _lib.MLA_ERR_INVALID_ARGUMENT
-    assert m(FAKE, FAKE, FAKE, 2, 513, FAKE, None, None) == _lib.MLA_ERR_UNSUPPORTED
+    # (partial_o, partial_lse, partial_slots, split_indptr, bs, rows, dv, out, lse, stream)
+    assert m(None, FAKE, 4, FAKE, 2, 16, 512, FAKE, None, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert m(FAKE, FAKE, 4, FAKE, 0, 16, 512, FAKE, None, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert m(FAKE, FAKE, -1, FAKE, 2, 16, 512, FAKE, None, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert m(FAKE, FAKE, 4, FAKE, 2, 513, 512, FAKE, None, None) == _lib.MLA_ERR_UNSUPPORTED
+    assert m(FAKE, FAKE, 4, FAKE, 2, 16, 256, FAKE, None, None) == _lib.MLA_ERR_UNSUPPORTED
+    assert m(P(0x1008), FAKE, 4, FAKE, 2, 16, 512, FAKE, None, None) == _lib.MLA_ERR_UNSUPPORTED
+    assert lib.mla_last_error_message().startswith(b"mla_merge_states")
 
 
 def test_table_and_plan_argument_errors():
