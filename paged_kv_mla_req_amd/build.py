@@ -35,7 +35,13 @@ COMMON_FLAGS = [
 # scores is a plain v_max/v_max3 (no operand canonicalisation).  No NaN
 # reaches it from the cache's unused slots: page tails are zero-filled, and
 # masked scores are -inf, scaled by a factor kept above 0.
-SOURCE_FLAGS = {"decode.hip": ["-fno-honor-nans"], "decode_tile.hip": ["-fno-honor-nans"]}
+# decode_tile.hip: uniform branches stay unstructured.  Structurizing them
+# (the default) keeps a branch's incoming values live through the other
+# side, e.g. the 256 accumulator registers through the block that clears
+# them, which doubles the kernel's register demand and spills.
+SOURCE_FLAGS = {"decode.hip": ["-fno-honor-nans"],
+                "decode_tile.hip": ["-fno-honor-nans", "-mllvm",
+                                    "-structurizecfg-skip-uniform-regions"]}
 
 
 def _hipcc() -> str:

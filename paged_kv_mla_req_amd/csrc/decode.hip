@@ -1367,6 +1367,8 @@ extern "C" mla_status mla_decode(const void* q, int32_t bs, int32_t q_len, int32
   if (num_parts > MLA_MAX_DECODE_PARTS)
     return fail(MLA_ERR_CAPACITY,
                 "mla_decode: num_parts above " + std::to_string(MLA_MAX_DECODE_PARTS));
+  if ((int64_t)bs * bt_row_stride >= (int64_t)1 << 29)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_decode: the block table must hold fewer than 2^29 entries");
   if ((int64_t)partial_slots < (int64_t)bs + num_parts)
     return fail(MLA_ERR_CAPACITY, "mla_decode: partial_slots must be at least bs + num_parts");
 

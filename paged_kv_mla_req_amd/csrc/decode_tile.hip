@@ -85,7 +85,6 @@ constexpr int kKSteps = kD / 16;       // 36 score MFMAs per tile
 constexpr int kPvMfmas = 2 * kGroups * kCTiles;  // 32 output MFMAs per tile
 constexpr int kLoadsPerWave = 9;       // 36 loads of 1 KiB per tile
 constexpr int kStores = 2 * kGroups * kCTiles;   // epilogue: 16-byte stores per lane
-constexpr int kQLoads = kKSteps;       // query loads of a piece
 constexpr float kTau = 8.0f;           // lazy-rescale threshold (log2 units)
 constexpr int kXcds = 8;
 
@@ -93,8 +92,10 @@ constexpr int kXcds = 8;
 // 15:14, lgkmcnt bits 11:8), the other counters untouched.
 constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 constexpr int lgkmcnt_imm(int n) { return 15 | (7 << 4) | (3 << 14) | (n << 8); }
-constexpr int vm_after(int q, int st) {
-  const int n = kLoadsPerWave + q * kQLoads + st * kStores;
+// vector memory operations issued after an interval's first tile load: its 9
+// tile loads and, when a piece's output was stored, 32 stores
+constexpr int vm_after(int st) {
+  const int n = kLoadsPerWave + st * kStores;
   return n > 63 ? 63 : n;
 }
 
@@ -134,6 +135,18 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// A pointer the same in every lane, as a value the compiler sees as uniform
+// (a buffer descriptor built from it then stays in scalar registers; from a
+// value it takes for divergent, every buffer access is wrapped in a loop over
+// the distinct descriptors).
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<T*>((uintptr_t)(((uint64_t)hi << 32) | lo));
+}
+
 __device__ __forceinline__ void mem_fence() { asm volatile("" ::: "memory"); }
 
 // Work-group barrier without a memory fence of the compiler's (which would
@@ -152,6 +165,12 @@ __device__ __forceinline__ uint32_t pinned(uint32_t x) {
   asm volatile("" : "+v"(x));
   return x;
 }
+// Holds a computed value at this point of the instruction stream: the
+// arithmetic that produces it cannot sink below (the compiler would otherwise
+// move the softmax out of the MFMA slots it is placed in, down to where its
+// results are stored).
+__device__ __forceinline__ void hold(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void hold(uint32_t& x) { asm volatile("" : "+v"(x)); }
 
 // This lane's index in its wave and its row and half, (n, h) = (lane % 32,
 // lane / 32), read afresh where they are used: the id passes through pinned(),
@@ -179,18 +198,44 @@ struct Part {
   int b_first, pg_first, b_last, pg_last, first_piece;
 };
 
-struct Seq {
-  int b;      // request
-  int t;      // tile of the request: keys 32 t .. 32 t + 31
-  int t_end;  // end of the request's tiles in the part
-  int L;      // the request's length
-  int piece;  // piece index inside the request
-  bool first; // first tile of the piece
-};
+// A tile's request word: bits 0..19 the request (the host keeps bs below
+// 2^20), bits 20..29 the keys of the request from the tile's first key on,
+// capped at 1023 (enough: with at most 512 rows, a tile whose count reaches
+// the cap has every key visible to every row), bit 30: the piece's first
+// tile, bit 31: its last.
+constexpr int kReqMask = (1 << 20) - 1;
+constexpr int kRemShift = 20;
+constexpr int kRemCap = 1023;
+constexpr int kFirstBit = 1 << 30;
+constexpr int kLastBit = (int)(1u << 31);
 
-__device__ __forceinline__ bool req_tiles(const Part& pt, const int32_t* seq_lens, int b, int& L,
+// Per-lane copies of request metadata, each read by one vector load: lane i
+// holds the value of request b0 + i (0 past the array).  The tile loop reads
+// them by v_readlane; a scalar load there would stall the wave for a memory
+// round trip whenever it misses the scalar cache.  Requests past the
+// 64-request window fall back to scalar loads.
+struct ReqWin {
+  int b0;
+  int32_t v;
+  const int32_t* src;
+};
+__device__ __forceinline__ ReqWin req_window(const int32_t* src, int n, int b0) {
+  ReqWin w;
+  w.b0 = b0;
+  w.src = src;
+  w.v = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(src), (short)0, 4 * n, 0x00020000),
+      4u * (uint32_t)(b0 + (int)lane_id()), 0, 0);
+  return w;
+}
+__device__ __forceinline__ int req_at(const ReqWin& w, int b) {
+  const int i = b - w.b0;
+  return (i >= 0 && i < 64) ? __builtin_amdgcn_readlane(w.v, i) : uniform_load(w.src, b);
+}
+
+__device__ __forceinline__ bool req_tiles(const Part& pt, const ReqWin& lens, int b, int& L,
                                           int& t0, int& t1) {
-  L = uniform_load(seq_lens, b);
+  L = req_at(lens, b);
   const int np = page_count(L);
   const int p0 = b == pt.b_first ? pt.pg_first : 0;
   const int p1 = b == pt.b_last ? min(pt.pg_last, np) : np;
@@ -199,51 +244,13 @@ __device__ __forceinline__ bool req_tiles(const Part& pt, const int32_t* seq_len
   return t1 > t0;
 }
 
-// Move s to the first tile of the first request >= b that has tiles in the
-// part (s is left as it is if there is none).
-__device__ __forceinline__ void seek(const Part& pt, const int32_t* seq_lens, int b, Seq& s) {
-  for (; b <= pt.b_last; ++b) {
-    int L, t0, t1;
-    if (req_tiles(pt, seq_lens, b, L, t0, t1)) {
-      s.b = b;
-      s.t = t0;
-      s.t_end = t1;
-      s.L = L;
-      s.first = true;
-      s.piece = (b == pt.b_first) ? pt.first_piece : 0;
-      return;
-    }
-  }
-}
-
-__device__ __forceinline__ void next_tile(const Part& pt, const int32_t* seq_lens, Seq& s) {
-  if (s.t + 1 < s.t_end) {
-    ++s.t;
-    s.first = false;
-  } else {
-    seek(pt, seq_lens, s.b + 1, s);
-  }
-}
-
-__device__ __forceinline__ bool last_of_piece(const Seq& s) { return s.t + 1 == s.t_end; }
-
-__device__ __forceinline__ int count_tiles(const Part& pt, const int32_t* seq_lens) {
+__device__ __forceinline__ int count_tiles(const Part& pt, const ReqWin& lens) {
   int n = 0;
   for (int b = pt.b_first; b <= pt.b_last; ++b) {
     int L, t0, t1;
-    if (req_tiles(pt, seq_lens, b, L, t0, t1)) n += t1 - t0;
+    if (req_tiles(pt, lens, b, L, t0, t1)) n += t1 - t0;
   }
   return n;
-}
-
-// Physical page of tile s, or -1 for a block-table entry outside the table
-// or the pool (the tile is then loaded as zeros and all its keys masked).
-__device__ __forceinline__ int64_t tile_page(const Seq& s, const int32_t* block_table,
-                                             const TileParams& P) {
-  const int p = s.t >> 1;
-  if (p >= P.bt_stride) return -1;
-  const int32_t e = uniform_load(block_table, (int64_t)s.b * P.bt_stride + p);
-  return (e >= 0 && e < P.num_pages) ? e : -1;
 }
 
 // Where the result of the piece of s goes: its partial slot (fp32 lse, bf16
@@ -251,24 +258,25 @@ __device__ __forceinline__ int64_t tile_page(const Seq& s, const int32_t* block_
 struct Dest {
   uint16_t* o;  // row 0 of the piece's 512-column rows
   float* lse;   // row 0 of its lse, or null
-  bool valid;
+  int64_t valid;  // the slot exists (64 bits: no padding bytes)
 };
 
-__device__ __forceinline__ Dest piece_dest(const Seq& s, const int32_t* split_indptr,
+__device__ __forceinline__ Dest piece_dest(int b, const Part& pt, const ReqWin& kbeg,
                                            uint16_t* partial_o, float* partial_lse,
                                            uint16_t* out, float* lse_out, const TileParams& P) {
-  const int k0 = uniform_load(split_indptr, s.b);
-  const int k = uniform_load(split_indptr, s.b + 1) - k0;
+  const int k0 = req_at(kbeg, b);
+  const int k = req_at(kbeg, b + 1) - k0;
+  const int piece = b == pt.b_first ? pt.first_piece : 0;
   Dest d;
   if (k > 1) {
-    const int64_t slot = (int64_t)k0 + s.piece;
+    const int64_t slot = (int64_t)k0 + piece;
     d.valid = slot >= 0 && slot < P.partial_slots;
     d.o = partial_o + slot * P.rows * kDv;
     d.lse = partial_lse + slot * P.rows;
   } else {
-    d.valid = true;
-    d.o = out + (int64_t)s.b * P.rows * kDv;
-    d.lse = lse_out ? lse_out + (int64_t)s.b * P.rows : nullptr;
+    d.valid = 1;
+    d.o = out + (int64_t)b * P.rows * kDv;
+    d.lse = lse_out ? lse_out + (int64_t)b * P.rows : nullptr;
   }
   return d;
 }
@@ -329,10 +337,11 @@ __device__ __forceinline__ uint32_t i_buf(int it) { return kIBase + (uint32_t)(i
 // the accumulator); the softmax reads the scores after 24 wait states; an
 // output tile is read by VALU code only after the chain's tail.
 //
-// Slots.  Variant kSP (scores of tile t and outputs of tile t-1): slots 0..51
-// hold the 36 score MFMAs and the output MFMAs m = 0..15 (k-step u = 0) at
-// slots 2 + 3m; slots 52..67 hold m = 16..31 (u = 1), with the softmax of
-// tile t spread over them.  kS: the 36 score MFMAs (the part's first tile);
+// Slots.  Variant kSP (scores of tile t and outputs of tile t-1): slots 0..43
+// hold the 36 score MFMAs and the output MFMAs m = 0..7 at slots 2 + 5m;
+// slots 44..67 hold m = 8..31, with the softmax of tile t spread over them
+// (it needs every score, and its arithmetic issues in the shadow of these
+// output MFMAs).  kS: the 36 score MFMAs (the part's first tile);
 // kP: the 32 output MFMAs (after the part's last tile).  Output MFMA m adds,
 // for k-step u = m / 16, column tile c = (m % 16) / 4 and row group
 // g = m % 4, V^T(c, u) P^T(g, u) to accumulator tile [g][c].
@@ -344,22 +353,25 @@ __device__ __forceinline__ uint32_t i_buf(int it) { return kIBase + (uint32_t)(i
 enum { kSP = 0, kS = 1, kP = 2 };
 constexpr int kAAhead = 6;
 constexpr int kARing = kAAhead + 1;
-constexpr int kHead = 52;   // slots of the score part of kSP
+constexpr int kHeadPv = 8;                 // output MFMAs among the score MFMAs
+constexpr int kPvStride = 5;               // ... one every kPvStride slots
+constexpr int kHead = kKSteps + kHeadPv;   // 44 slots of the score part of kSP
 constexpr int kVLead = 3;   // value reads go out this many slots ahead
 
 __host__ __device__ constexpr int n_slots(int var) {
-  return var == kSP ? kHead + kPvMfmas / 2 : var == kS ? kKSteps : kPvMfmas;
+  return var == kSP ? kKSteps + kPvMfmas : var == kS ? kKSteps : kPvMfmas;
 }
 __host__ __device__ constexpr bool is_pv(int var, int s) {
   return var == kS   ? false
          : var == kP ? true
-                     : (s >= kHead || (s >= 2 && (s - 2) % 3 == 0 && (s - 2) / 3 < kPvMfmas / 2));
+                     : (s >= kHead || (s >= 2 && (s - 2) % kPvStride == 0 &&
+                                          (s - 2) / kPvStride < kHeadPv));
 }
 __host__ __device__ constexpr bool has_s(int var) { return var != kP; }
 __host__ __device__ constexpr bool has_pv(int var) { return var != kS; }
 
 // The schedule of a variant, worked out once at compile time.
-constexpr int kMaxSlots = kHead + kPvMfmas / 2;  // 68
+constexpr int kMaxSlots = kKSteps + kPvMfmas;  // 68
 struct Sched {
   int n;
   bool pv[kMaxSlots];        // slot holds an output MFMA
@@ -621,13 +633,12 @@ __device__ __forceinline__ void slots(std::integer_sequence<int, S...>, f32x16& 
   (slot<VAR, PV_ZERO, S>(s, o, R, A, qreg, hook, pay), ...);
 }
 
+// The chain's slots; the caller has issued its first reads (issue_reads<VAR,
+// -1>) into R.
 template <int VAR, bool PV_ZERO, typename Hook, typename Pay>
-__device__ __forceinline__ void chain(f32x16& s, f32x16 (&o)[kGroups][kCTiles],
+__device__ __forceinline__ void chain(f32x16& s, f32x16 (&o)[kGroups][kCTiles], ChainRegs& R,
                                       const ChainAddr& A, const bf16x8 (&qreg)[kKSteps],
                                       Hook&& hook, Pay&& pay) {
-  ChainRegs R;
-  SB();
-  issue_reads<VAR, -1>(R, A);
   SB();
   slots<VAR, PV_ZERO>(std::make_integer_sequence<int, n_slots(VAR)>{}, s, o, R, A, qreg, hook,
                       pay);
@@ -736,14 +747,14 @@ __device__ __forceinline__ void tile_loads(std::integer_sequence<int, K...>, con
   (tile_load<K>(tl, w, voff), ...);
 }
 
-// The slots after which the tile loads go out: every sixth slot of the score
+// The slots after which the tile loads go out: every fifth slot of the score
 // part (kSP), every fourth score MFMA (kS).
 __host__ __device__ constexpr int load_at(int var, int s) {
-  if (var == kSP) return (s % 6 == 3 && s / 6 < kLoadsPerWave) ? s / 6 : -1;
+  if (var == kSP) return (s % 5 == 3 && s / 5 < kLoadsPerWave) ? s / 5 : -1;
   if (var == kS) return (s % 4 == 3) ? s / 4 : -1;
   return -1;
 }
-static_assert(load_at(kSP, 6 * 8 + 3) == 8 && 6 * 8 + 3 < kHead && load_at(kS, 35) == 8,
+static_assert(load_at(kSP, 5 * 8 + 3) == 8 && 5 * 8 + 3 < kHead && load_at(kS, 35) == 8,
               "9 tile loads per chain");
 
 // ---------------------------------------------------------------------------
@@ -779,7 +790,10 @@ mla_decode_tile_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
   if (npages <= 0 || pt.b_first < 0 || pt.b_last >= P.bs || pt.b_first > pt.b_last ||
       pt.pg_first < 0 || pt.pg_last < 0 || pt.first_piece < 0)
     return;
-  const int T = count_tiles(pt, seq_lens);
+  // the lengths and first partial slots of the part's first 64 requests
+  const ReqWin lens0 = req_window(seq_lens, P.bs, pt.b_first);
+  const ReqWin kbeg = req_window(split_indptr, P.bs + 1, pt.b_first);
+  const int T = count_tiles(pt, lens0);
   if (T <= 0) return;
 
   const int rb0 = blockIdx.y * kRowsPerBlock;  // the block's first row
@@ -794,27 +808,59 @@ mla_decode_tile_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
   __builtin_amdgcn_s_waitcnt(lgkmcnt_imm(0));
   barrier();
 
-  // ---- tile loads: the tile whose loads go out next, its page read one
-  // interval ahead (a block-table entry through the scalar cache)
-  Seq ld;
-  seek(pt, seq_lens, pt.b_first, ld);
-  int ld_done = 0;
-  int64_t ld_page = tile_page(ld, block_table, P);
+  // ---- the part's tiles, 64 at a time: lane j of the window describes tile
+  // w0 + j of the part (the tiles in the order they run)
+  //   w_tok: pool index of the tile's first key, page * 64 + 32 (t % 2), or -1
+  //          when the block-table entry is outside the table or the pool (the
+  //          tile then loads as zeros and all its keys are masked)
+  //   w_bf:  its request word (request, remaining keys, first / last of piece)
+  // The window is rebuilt when the tile loads reach its end (starting one
+  // tile behind the score tile, so the four tiles in use stay inside).
+  int32_t w_tok = -1, w_bf = 0;
+  int w0 = 0;
+  const int bt_bytes = 4 * P.bs * P.bt_stride;  // < 2^31: checked by the host
+  auto load_window = [&](int base, const ReqWin& lens) __attribute__((always_inline)) {
+    const int j = base + (int)lane_id();
+    int bf = 0, addr = -1, half = 0, off = 0;
+    for (int b = pt.b_first; b <= pt.b_last && off < base + 64; ++b) {
+      int L, t0, t1;
+      if (!req_tiles(pt, lens, b, L, t0, t1)) continue;
+      const int nt = t1 - t0, k = j - off;
+      if (k >= 0 && k < nt) {
+        const int t = t0 + k;
+        bf = b | (min(L - kTileKeys * t, kRemCap) << kRemShift) | (k == 0 ? kFirstBit : 0) |
+             (k == nt - 1 ? kLastBit : 0);
+        half = t & 1;
+        addr = (t >> 1) < P.bt_stride ? b * P.bt_stride + (t >> 1) : -1;
+      }
+      off += nt;
+    }
+    const int32_t e = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(block_table), (short)0, bt_bytes,
+                                          0x00020000),
+        addr >= 0 ? 4u * (uint32_t)addr : 0x80000000u, 0, 0);
+    w_tok = (addr >= 0 && e >= 0 && e < P.num_pages) ? e * kPage + half * kTileKeys : -1;
+    w_bf = bf;
+  };
+  load_window(0, lens0);
+  auto w_at = [&](int32_t v, int i) __attribute__((always_inline)) {
+    return __builtin_amdgcn_readlane(v, i - w0);
+  };
+
+  // ---- tile loads: the descriptor of tile `it`'s loads (empty past the last tile)
   auto next_load = [&](int it) __attribute__((always_inline)) {
     TileLoad tl;
     const uint8_t* src = kv;
     int valid = 0;
-    if (ld_done < T) {
-      if (ld_page >= 0) {
-        src = kv + ld_page * (int64_t)(kPage * kRowBytes) + (ld.t & 1) * (kTileKeys * kRowBytes);
-        valid = min(kTileKeys, max(0, ld.L - kTileKeys * ld.t));
-      }
-      ++ld_done;
-      if (ld_done < T) {
-        next_tile(pt, seq_lens, ld);
-        ld_page = tile_page(ld, block_table, P);
+    if (it < T) {
+      const int tok = w_at(w_tok, it);
+      if (tok >= 0) {
+        src = kv + (int64_t)tok * kRowBytes;
+        valid = min(kTileKeys, (w_at(w_bf, it) >> kRemShift) & kRemCap);
       }
     }
+    src = uniform_ptr(src);
+    valid = __builtin_amdgcn_readfirstlane(valid);
     tl.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(src), (short)0,
                                                 valid * kRowBytes, 0x00020000);
     tl.vslot = smem_base + v_slot(it);
@@ -823,19 +869,20 @@ mla_decode_tile_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
   };
 
   // ---- queries of the first piece, tiles 0 and 1
-  Seq sq;  // the tile whose scores run
-  seek(pt, seq_lens, pt.b_first, sq);
   bf16x8 qreg[kKSteps];
+  // The queries of request b: one buffer over the request's rows, one lane
+  // offset and 36 immediate offsets (rows past the last read as zeros).
   auto load_q = [&](int b) __attribute__((always_inline)) {
-    const uint16_t* qb = q + (int64_t)b * P.rows * kD;  // the request's first row
+    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(const_cast<uint16_t*>(q) + (int64_t)b * P.rows * kD), (short)0,
+        P.rows * kD * (int)sizeof(uint16_t), 0x00020000);
     const Lane ln = lane_now();
-    const int r = ws0 + ln.n;
-    const uint32_t qoff = (uint32_t)(r < P.rows ? r : 0) * kD + 8 * ln.h;  // past the end: row 0
+    const uint32_t qoff = ((uint32_t)(ws0 + ln.n) * kD + 8 * ln.h) * 2;
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks)
-      qreg[ks] = *reinterpret_cast<const bf16x8*>(qb + (qoff + 16 * ks));
+      qreg[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, qoff, 32 * ks, 0));
   };
-  load_q(sq.b);
+  load_q(w_at(w_bf, 0) & kReqMask);
   {
     const uint32_t voff = load_off(lane_now().lane, wave);
     const TileLoad t0 = next_load(0);
@@ -847,66 +894,30 @@ mla_decode_tile_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerWave));
   barrier();
 
-  Seq os = sq;  // the tile whose output MFMAs run (one behind)
   f32x16 o[kGroups][kCTiles];
   float m_run = -INFINITY, l_run = 0.f;
-  bool q_loaded = false;  // this interval loaded the next piece's queries
   bool stored = false;    // this interval stored a piece's output
 
   // One interval: scores of tile `it` (it < T) and outputs of tile it-1
   // (it >= 1).  VAR: kS (the first tile), kSP, or kP (after the last tile).
   auto interval = [&](int it, auto var_tag) __attribute__((always_inline)) {
     constexpr int VAR = decltype(var_tag)::value;
-    q_loaded = stored = false;
+    stored = false;
     const Lane ln = lane_now();
     const int n = ln.n, h = ln.h, r = ws0 + n;  // r: this lane's score row
-    const TileLoad tl = has_s(VAR) ? next_load(it + 2) : TileLoad{};
-    // the output tile's piece ends with it: its destination and scales
-    const bool out_last = has_pv(VAR) && last_of_piece(os);
-    Dest d = {};
-    if (out_last) d = piece_dest(os, split_indptr, partial_o, partial_lse, out, lse_out, P);
-    // the score tile: its mask and its piece
-    const bool s_first = has_s(VAR) && sq.first;
-    const bool s_last = has_s(VAR) && last_of_piece(sq);
-    const bool more = has_s(VAR) && it + 1 < T;
-    int vis = 16;
-    if (has_s(VAR)) {
-      const int key0 = kTileKeys * sq.t;
-      const int lim_min = P.causal ? sq.L - P.q_len + i_tok_min : sq.L - 1;
-      const bool bad_page = tile_page(sq, block_table, P) < 0;
-      if (bad_page || key0 + kTileKeys - 1 > lim_min) {
-        const int i_tok = r < P.rows ? r / P.heads : 0;
-        const int lim = P.causal ? sq.L - P.q_len + i_tok : sq.L - 1;
-        vis = bad_page ? 0 : min(16, lim - (key0 + 16 * h) + 1);
-      }
-      if (s_first) {
-        m_run = -INFINITY;
-        l_run = 0.f;
-      }
+    if (has_s(VAR) && it + 2 < T && it + 2 - w0 >= 64) {
+      w0 = it - 1;  // rare: every 61 tiles
+      load_window(w0, req_window(seq_lens, P.bs, pt.b_first));
     }
-    Seq nx = sq;
-    if (s_last && more) next_tile(pt, seq_lens, nx);
-    // ---- the output tile starts a piece: clear the accumulators; else
-    // rescale them by the factors of tile it-1 (rows whose running max
-    // moved) before its terms are added
-    if (has_pv(VAR) && os.first) {
-      zero_acc(o);
-    } else if constexpr (has_pv(VAR)) {
-      // the factors of the four row groups, [n][g]; read and waited for in one
-      // statement (the compiler would make a read it can see wait for the
-      // tile loads in flight)
-      f32x4 al;
-      asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)"
-                   : "=v"(al)
-                   : "v"(smem_base + a_buf(it - 1) + 16 * n));
-      if (__any(al[0] != 1.0f || al[1] != 1.0f || al[2] != 1.0f || al[3] != 1.0f)) {
-#pragma unroll
-        for (int g = 0; g < kGroups; ++g)
-#pragma unroll
-          for (int c = 0; c < kCTiles; ++c) scale_tile(o[g][c], al[g]);
-      }
-    }
-    // ---- the chain
+    // the output tile (it-1): the first of its piece starts from zero
+    // accumulators
+    const int pbf = has_pv(VAR) ? w_at(w_bf, it - 1) : 0;
+    const bool o_first = has_pv(VAR) && (pbf & kFirstBit);
+    const bool out_last = has_pv(VAR) && (pbf & kLastBit);
+    if (o_first) zero_acc(o);
+    // ---- the LDS reads go out first (the rescale factors of tile it-1, then
+    // the chain's first operands); the interval's set-up runs in the shadow
+    // of the first MFMAs
     ChainAddr A;
     const uint32_t vb = smem_base + v_slot(it);
 #pragma unroll
@@ -920,30 +931,98 @@ mla_decode_tile_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
       A.va[1][1] = A.va[1][0] ^ 64u;
     }
     A.pb = smem_base + p_buf(it - 1) + 16 * ln.lane;
+    ChainRegs R;
+    // the factors of the four row groups, [n][g] (older than every chain
+    // read: the chain's first wait covers it)
+    f32x4 al;
+    SB();
+    if constexpr (has_pv(VAR))
+      asm volatile("ds_read_b128 %0, %1" : "=&v"(al) : "v"(smem_base + a_buf(it - 1) + 16 * n));
+    SB();
+    issue_reads<VAR, -1>(R, A);
+    SB();
+    // rescale the accumulators by the factors of tile it-1 (rows whose
+    // running max moved) before its terms are added
+    auto rescale = [&]() __attribute__((always_inline)) {
+      if (!o_first &&
+          __any(al[0] != 1.0f || al[1] != 1.0f || al[2] != 1.0f || al[3] != 1.0f)) {
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+          for (int c = 0; c < kCTiles; ++c) scale_tile(o[g][c], al[g]);
+      }
+    };
+    if constexpr (VAR == kP) {
+      // the first output MFMA is the chain's first: wait for the factors here
+      lgkm_wait<0>();
+      rescale();
+    }
+    // the score tile (it): its piece, its mask, the loads of tile it+2
+    TileLoad tl{};
+    int sbf = 0, vis = 16;
+    bool s_first = false, s_last = false, more = false, defer = false;
+    bool partial = false;  // some key of the tile is hidden from some row of the wave
+    auto setup_s = [&]() __attribute__((always_inline)) {
+      sbf = w_at(w_bf, it);
+      s_first = sbf & kFirstBit;
+      s_last = sbf & kLastBit;
+      more = it + 1 < T;
+      // at a piece's end the tile loads wait until the next piece's queries
+      // have gone out (after the chain)
+      defer = s_last && more;
+      tl = next_load(it + 2);
+    };
+    auto setup_mask = [&]() __attribute__((always_inline)) {
+      // last visible key of the wave's first row, relative to the tile's first key
+      const int rem = (sbf >> kRemShift) & kRemCap;
+      const int lim_min = P.causal ? rem - P.q_len + i_tok_min : rem - 1;
+      const bool bad_page = w_at(w_tok, it) < 0;
+      partial = bad_page || kTileKeys - 1 > lim_min;
+      if (partial) {
+        const int i_tok = r < P.rows ? r / P.heads : 0;
+        const int lim = P.causal ? rem - P.q_len + i_tok : rem - 1;
+        vis = bad_page ? 0 : min(16, lim - 16 * h + 1);
+      }
+      if (s_first) {
+        m_run = -INFINITY;
+        l_run = 0.f;
+      }
+    };
     const uint32_t voff = load_off(ln.lane, wave);
     f32x16 s;
     float ls = 0.f, alpha = 1.0f;
     uint32_t pk[8];
     auto hook = [&](auto sc) __attribute__((always_inline)) {
       constexpr int S = decltype(sc)::value;
-      if constexpr (load_at(VAR, S) >= 0) tile_load<load_at(VAR, S)>(tl, wave, voff);
+      if constexpr (load_at(VAR, S) >= 0) {
+        if (!defer) tile_load<load_at(VAR, S)>(tl, wave, voff);
+      }
     };
-    // the softmax of the score tile, in the shadow of the output MFMAs of
-    // slots kHead .. kHead+15 (kSP); after the chain for kS
+    // the softmax of the score tile, in the shadow of the output MFMAs of the
+    // tail slots kHead .. kHead+20 (kSP); after the chain for kS
     float mx = 0.f, m_tile = 0.f, neg_m = 0.f;
     auto soft = [&](auto step) __attribute__((always_inline)) {
       constexpr int k = decltype(step)::value;
       if constexpr (k == 0) {
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");  // the last score MFMA's result
+        if (partial) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] = i < vis ? s[i] : -INFINITY;
+          for (int i = 0; i < 16; ++i) {
+            float x = i < vis ? s[i] : -INFINITY;
+            hold(x);
+            s[i] = x;
+          }
+        }
       } else if constexpr (k == 1) {
         mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
                    fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+        hold(mx);
+      } else if constexpr (k == 2) {
         mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])),
                              fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]))));
-      } else if constexpr (k == 2) {
         m_tile = c_log2 * xhalf_max(mx);
+        hold(m_tile);
+      } else if constexpr (k == 3) {
         // lazy rescale: move the running max only when the tile's max exceeds
         // it by more than kTau (weights stay <= 2^kTau otherwise)
         const bool need = m_tile > m_run + kTau;
@@ -951,33 +1030,55 @@ mla_decode_tile_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
         alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
         m_run = m_new;
         neg_m = m_run == -INFINITY ? 0.f : -m_run;  // -inf: no visible key yet
-      } else if constexpr (k >= 3 && k < 11) {
-        constexpr int i = 2 * (k - 3);
+        hold(alpha);
+        hold(m_run);
+        hold(neg_m);
+      } else if constexpr (k >= 4 && k < 12) {
+        constexpr int i = 2 * (k - 4);
         const float p0 = __builtin_amdgcn_exp2f(fmaf(s[i], c_log2, neg_m));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(s[i + 1], c_log2, neg_m));
         ls += p0 + p1;
         pk[i >> 1] =
             __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p0, p1}, bf16x2));
-      } else if constexpr (k == 11) {
+        hold(pk[i >> 1]);
+        hold(ls);
+      } else if constexpr (k == 12) {
         l_run = l_run * alpha + ls;
+        hold(l_run);
       }
     };
+    // the tail slot of each softmax step (kSP): the exponentials every other slot
     auto pay = [&](auto sc) __attribute__((always_inline)) {
-      constexpr int S = decltype(sc)::value;
-      if constexpr (VAR == kSP && S >= kHead && S < kHead + 12) soft(ic<S - kHead>{});
+      constexpr int X = decltype(sc)::value;
+      if constexpr (X == 0 && has_s(VAR)) setup_s();
+      if constexpr (X == 1 && VAR == kSP) rescale();  // the first output MFMA is at slot 2
+      if constexpr (X == 4 && has_s(VAR)) setup_mask();
+      constexpr int S = X - kHead;
+      if constexpr (VAR == kSP) {
+        if constexpr (S == 0) soft(ic<0>{});
+        if constexpr (S == 1) soft(ic<1>{});
+        if constexpr (S == 2) soft(ic<2>{});
+        if constexpr (S == 3) soft(ic<3>{});
+        if constexpr (S >= 5 && S <= 19 && (S - 5) % 2 == 0) soft(ic<4 + (S - 5) / 2>{});
+        if constexpr (S == 20) soft(ic<12>{});
+      }
     };
-    chain<VAR, false>(s, o, A, qreg, hook, pay);
+    chain<VAR, false>(s, o, R, A, qreg, hook, pay);
     if constexpr (VAR == kS) {
       soft(ic<0>{});
       soft(ic<1>{}); soft(ic<2>{}); soft(ic<3>{}); soft(ic<4>{}); soft(ic<5>{});
       soft(ic<6>{}); soft(ic<7>{}); soft(ic<8>{}); soft(ic<9>{}); soft(ic<10>{});
-      soft(ic<11>{});
+      soft(ic<11>{}); soft(ic<12>{});
     }
     if constexpr (has_s(VAR)) {
       // ---- the next piece's queries (the score MFMAs have read these)
       if (s_last && more) {
-        load_q(nx.b);
-        q_loaded = true;
+        load_q(w_at(w_bf, it + 1) & kReqMask);
+        // this interval's tile loads after the queries (kept in that order):
+        // the wait for the next tile at the interval's end then covers the
+        // queries too
+        SB();
+        tile_loads(std::make_integer_sequence<int, kLoadsPerWave>{}, tl, wave, voff);
       }
       // ---- hand the weights and the rescale factors to every wave
       // (LDS writes from assembly too: the compiler would make a write it
@@ -996,7 +1097,7 @@ mla_decode_tile_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
                      : "memory");
       if (s_last) {
         // ---- the score tile ends its piece: lse and the output scale
-        const Dest ds = piece_dest(sq, split_indptr, partial_o, partial_lse, out, lse_out, P);
+        const Dest ds = piece_dest(sbf & kReqMask, pt, kbeg, partial_o, partial_lse, out, lse_out, P);
         const float l_tot = xhalf_sum(l_run);
         const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
         const float lse_val =
@@ -1012,6 +1113,9 @@ mla_decode_tile_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
     if constexpr (has_pv(VAR)) {
       // ---- the output tile ends its piece: store all 128 rows of this
       // wave's 128 columns
+      const Dest d = out_last ? piece_dest(pbf & kReqMask, pt, kbeg, partial_o, partial_lse, out,
+                                           lse_out, P)
+                              : Dest{};
       if (out_last && d.valid) {
         f32x4 inv;
         asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)"
@@ -1019,7 +1123,7 @@ mla_decode_tile_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
                      : "v"(smem_base + i_buf(it - 1) + 16 * n));
         // the block's rows of the piece; the range ends with the request's last row
         const __amdgpu_buffer_rsrc_t dst = __builtin_amdgcn_make_buffer_rsrc(
-            d.o + (int64_t)rb0 * kDv, (short)0, (P.rows - rb0) * kDv * (int)sizeof(uint16_t),
+            uniform_ptr(d.o + (int64_t)rb0 * kDv), (short)0, (P.rows - rb0) * kDv * (int)sizeof(uint16_t),
             0x00020000);
 #pragma unroll
         for (int g = 0; g < kGroups; ++g) {
@@ -1032,30 +1136,20 @@ mla_decode_tile_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
         }
         stored = true;
       }
-      next_tile(pt, seq_lens, os);
-    }
-    if constexpr (has_s(VAR)) {
-      sq = nx;
-      if (!(s_last && more)) next_tile(pt, seq_lens, sq);
     }
   };
 
-  // The end of interval `it` (< T): tile it+1 landed (the loads issued after
-  // its loads are this interval's 9 and, at a piece's end, the next queries or
-  // the outputs stored after them), the weights, factors and scales are in
-  // LDS; then the barrier.
+  // The end of interval `it` (< T): tile it+1 and, at a piece's end, the next
+  // queries landed (what was issued after them is this interval's 9 tile
+  // loads and, when a piece ended, the 32 output stores), the weights,
+  // factors and scales are in LDS; then the barrier.
   auto sync = [&]() __attribute__((always_inline)) {
-    if (q_loaded && stored)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(vm_after(1, 1)));
-    else if (q_loaded)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(vm_after(1, 0)));
-    else if (stored)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(vm_after(0, 1)));
+    if (stored)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(vm_after(1)));
     else
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(vm_after(0, 0)));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(vm_after(0)));
     __builtin_amdgcn_s_waitcnt(lgkmcnt_imm(0));
     barrier();
-    if (q_loaded) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the queries landed
   };
   interval(0, ic<kS>{});
   sync();
