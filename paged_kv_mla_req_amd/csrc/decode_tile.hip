@@ -337,11 +337,10 @@ __device__ __forceinline__ uint32_t i_buf(int it) { return kIBase + (uint32_t)(i
 // the accumulator); the softmax reads the scores after 24 wait states; an
 // output tile is read by VALU code only after the chain's tail.
 //
-// Slots.  Variant kSP (scores of tile t and outputs of tile t-1): slots 0..43
-// hold the 36 score MFMAs and the output MFMAs m = 0..7 at slots 2 + 5m;
-// slots 44..67 hold m = 8..31, with the softmax of tile t spread over them
-// (it needs every score, and its arithmetic issues in the shadow of these
-// output MFMAs).  kS: the 36 score MFMAs (the part's first tile);
+// Slots.  Variant kSP (scores of tile t and outputs of tile t-1): slots 0..35
+// hold the 36 score MFMAs, slots 36..67 the 32 output MFMAs, with the softmax
+// of tile t spread over them (it needs every score, and its arithmetic
+// issues in the shadow of these output MFMAs).  kS: the 36 score MFMAs (the part's first tile);
 // kP: the 32 output MFMAs (after the part's last tile).  Output MFMA m adds,
 // for k-step u = m / 16, column tile c = (m % 16) / 4 and row group
 // g = m % 4, V^T(c, u) P^T(g, u) to accumulator tile [g][c].
@@ -353,9 +352,7 @@ __device__ __forceinline__ uint32_t i_buf(int it) { return kIBase + (uint32_t)(i
 enum { kSP = 0, kS = 1, kP = 2 };
 constexpr int kAAhead = 6;
 constexpr int kARing = kAAhead + 1;
-constexpr int kHeadPv = 8;                 // output MFMAs among the score MFMAs
-constexpr int kPvStride = 5;               // ... one every kPvStride slots
-constexpr int kHead = kKSteps + kHeadPv;   // 44 slots of the score part of kSP
+constexpr int kHead = kKSteps;  // 36 slots of the score part of kSP
 constexpr int kVLead = 3;   // value reads go out this many slots ahead
 
 __host__ __device__ constexpr int n_slots(int var) {
@@ -364,8 +361,7 @@ __host__ __device__ constexpr int n_slots(int var) {
 __host__ __device__ constexpr bool is_pv(int var, int s) {
   return var == kS   ? false
          : var == kP ? true
-                     : (s >= kHead || (s >= 2 && (s - 2) % kPvStride == 0 &&
-                                          (s - 2) / kPvStride < kHeadPv));
+                     : s >= kHead;
 }
 __host__ __device__ constexpr bool has_s(int var) { return var != kP; }
 __host__ __device__ constexpr bool has_pv(int var) { return var != kS; }
@@ -747,14 +743,12 @@ __device__ __forceinline__ void tile_loads(std::integer_sequence<int, K...>, con
   (tile_load<K>(tl, w, voff), ...);
 }
 
-// The slots after which the tile loads go out: every fifth slot of the score
-// part (kSP), every fourth score MFMA (kS).
+// The slots after which the tile loads go out: every fourth score MFMA.
 __host__ __device__ constexpr int load_at(int var, int s) {
-  if (var == kSP) return (s % 5 == 3 && s / 5 < kLoadsPerWave) ? s / 5 : -1;
-  if (var == kS) return (s % 4 == 3) ? s / 4 : -1;
+  if (var == kSP || var == kS) return (s % 4 == 3 && s / 4 < kLoadsPerWave) ? s / 4 : -1;
   return -1;
 }
-static_assert(load_at(kSP, 5 * 8 + 3) == 8 && 5 * 8 + 3 < kHead && load_at(kS, 35) == 8,
+static_assert(load_at(kSP, 35) == 8 && 35 < kHead && load_at(kS, 35) == 8,
               "9 tile loads per chain");
 
 // ---------------------------------------------------------------------------
@@ -999,7 +993,7 @@ mla_decode_tile_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
       }
     };
     // the softmax of the score tile, in the shadow of the output MFMAs of the
-    // tail slots kHead .. kHead+20 (kSP); after the chain for kS
+    // tail slots kHead .. kHead+27 (kSP); after the chain for kS
     float mx = 0.f, m_tile = 0.f, neg_m = 0.f;
     auto soft = [&](auto step) __attribute__((always_inline)) {
       constexpr int k = decltype(step)::value;
@@ -1047,11 +1041,11 @@ mla_decode_tile_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
         hold(l_run);
       }
     };
-    // the tail slot of each softmax step (kSP): the exponentials every other slot
+    // the tail slot of each softmax step (kSP): the exponentials every third slot
     auto pay = [&](auto sc) __attribute__((always_inline)) {
       constexpr int X = decltype(sc)::value;
       if constexpr (X == 0 && has_s(VAR)) setup_s();
-      if constexpr (X == 1 && VAR == kSP) rescale();  // the first output MFMA is at slot 2
+      if constexpr (X == 1 && VAR == kSP) rescale();  // before the first output MFMA
       if constexpr (X == 4 && has_s(VAR)) setup_mask();
       constexpr int S = X - kHead;
       if constexpr (VAR == kSP) {
@@ -1059,8 +1053,8 @@ mla_decode_tile_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict
         if constexpr (S == 1) soft(ic<1>{});
         if constexpr (S == 2) soft(ic<2>{});
         if constexpr (S == 3) soft(ic<3>{});
-        if constexpr (S >= 5 && S <= 19 && (S - 5) % 2 == 0) soft(ic<4 + (S - 5) / 2>{});
-        if constexpr (S == 20) soft(ic<12>{});
+        if constexpr (S >= 5 && S <= 26 && (S - 5) % 3 == 0) soft(ic<4 + (S - 5) / 3>{});
+        if constexpr (S == 27) soft(ic<12>{});
       }
     };
     chain<VAR, false>(s, o, R, A, qreg, hook, pay);
