@@ -121,7 +121,7 @@ def _kernel_of(kv_dtype: str):
     """(source file under csrc/, kernel name) of the decode kernel that runs
     for a cache dtype."""
     if kv_dtype == "bf16":
-        return "decode_tile.hip", "mla_decode_tile_kernel"
+        return "decode.hip", "mla_decode_kernel<false>"
     return "decode.hip", "mla_decode_kernel<true>"
 
 

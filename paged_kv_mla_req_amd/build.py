@@ -19,8 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmla_decode.so")
-SOURCES = ["abi.hip", "block_table.hip", "plan.hip", "decode.hip", "decode_tile.hip", "merge.hip",
-           "append.hip"]
+SOURCES = ["abi.hip", "block_table.hip", "plan.hip", "decode.hip", "merge.hip", "append.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms stay disabled: the compiler would otherwise emit
@@ -35,13 +34,7 @@ COMMON_FLAGS = [
 # scores is a plain v_max/v_max3 (no operand canonicalisation).  No NaN
 # reaches it from the cache's unused slots: page tails are zero-filled, and
 # masked scores are -inf, scaled by a factor kept above 0.
-# decode_tile.hip: uniform branches stay unstructured.  Structurizing them
-# (the default) keeps a branch's incoming values live through the other
-# side, e.g. the 256 accumulator registers through the block that clears
-# them, which doubles the kernel's register demand and spills.
-SOURCE_FLAGS = {"decode.hip": ["-fno-honor-nans"],
-                "decode_tile.hip": ["-fno-honor-nans", "-mllvm",
-                                    "-structurizecfg-skip-uniform-regions"]}
+SOURCE_FLAGS = {"decode.hip": ["-fno-honor-nans"]}
 
 
 def _hipcc() -> str:

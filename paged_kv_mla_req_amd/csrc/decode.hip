@@ -54,7 +54,6 @@
 #include <hip/hip_ext.h>
 
 #include "common.h"
-#include "decode_tile.h"
 
 namespace mla {
 
@@ -1382,21 +1381,6 @@ extern "C" mla_status mla_decode(const void* q, int32_t bs, int32_t q_len, int32
   p.rows = (int32_t)rows;
   p.causal = causal ? 1 : 0;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
-  if (kv_dtype == MLA_KV_BF16) {
-    TileParams pp;
-    pp.num_pages = num_pages;
-    pp.partial_slots = partial_slots;
-    pp.bt_stride = bt_row_stride;
-    pp.bs = bs;
-    pp.q_len = q_len;
-    pp.heads = num_heads;
-    pp.rows = (int32_t)rows;
-    pp.causal = causal ? 1 : 0;
-    pp.scale_log2 = softmax_scale * 1.4426950408889634f;
-    return launch_tile_decode(q, kv_cache, block_table, seq_lens, tile_plan, num_parts,
-                              split_indptr, partial_o, partial_lse, out, lse, pp, stream,
-                              ev_start, ev_stop);
-  }
   dim3 grid(num_parts, (unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
   auto launch = [&](auto kernel, const float* descale) {
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(q);
@@ -1412,6 +1396,9 @@ extern "C" mla_status mla_decode(const void* q, int32_t bs, int32_t q_len, int32
                          seq_lens, tile_plan, split_indptr, descale, po, partial_lse, op,
                          lse, p);
   };
-  launch(mla_decode_kernel<true>, kv_descale);
+  if (kv_dtype == MLA_KV_FP8_E4M3)
+    launch(mla_decode_kernel<true>, kv_descale);
+  else
+    launch(mla_decode_kernel<false>, nullptr);
   return check_launch("mla_decode");
 }

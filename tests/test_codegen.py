@@ -179,35 +179,23 @@ def decode_asm():
     return _compile("decode.hip")
 
 
-@pytest.fixture(scope="module")
-def tile_asm():
-    return _compile("decode_tile.hip")
+def test_both_kernels_present(decode_asm):
+    """The page kernel in its two instances: bf16 cache and e4m3 cache."""
+    names = list(_kernels(decode_asm))
+    assert len(names) == 2, names
 
 
-def _all_kernels(decode_asm, tile_asm):
-    k = dict(_kernels(decode_asm))
-    k.update(_kernels(tile_asm, "mla_decode_tile_kernel"))
-    return k
-
-
-def test_kernels_present(decode_asm, tile_asm):
-    assert len(_kernels(decode_asm)) == 1, list(_kernels(decode_asm))
-    assert len(_kernels(tile_asm, "mla_decode_tile_kernel")) == 1
-
-
-def test_no_instruction_touches_an_in_flight_lds_read(decode_asm, tile_asm):
-    for name, instrs in _all_kernels(decode_asm, tile_asm).items():
+def test_no_instruction_touches_an_in_flight_lds_read(decode_asm):
+    for name, instrs in _kernels(decode_asm).items():
         bad = _check(instrs)
         assert not bad, f"{name}: {len(bad)} instructions touch in-flight registers, e.g. {bad[:5]}"
 
 
-def test_tile_kernel_has_no_spills(tile_asm):
-    """The tile kernel keeps every value in registers: no VGPR spills and no
-    scratch memory (a spill reload would also wait on every tile load in
-    flight)."""
-    sp = re.search(r"\.vgpr_spill_count:\s+(\d+)", tile_asm)
-    assert sp and int(sp.group(1)) == 0
-    assert "scratch_" not in tile_asm
+def test_decode_kernels_have_no_scratch(decode_asm):
+    """Every value stays in registers: no VGPR spills and no scratch memory (a
+    spill reload would also wait on every page load in flight)."""
+    assert all(int(n) == 0 for n in re.findall(r"\.vgpr_spill_count:\s+(\d+)", decode_asm))
+    assert "scratch_" not in decode_asm
 
 
 def test_checker_flags_a_planted_use():
@@ -230,8 +218,8 @@ def test_checker_flags_a_planted_use():
     assert _check(smem_drained) == []
 
 
-def test_no_unguarded_mfma_hazard(decode_asm, tile_asm):
-    for name, instrs in _all_kernels(decode_asm, tile_asm).items():
+def test_no_unguarded_mfma_hazard(decode_asm):
+    for name, instrs in _kernels(decode_asm).items():
         bad = _mfma_hazards(instrs)
         assert not bad, f"{name}: {len(bad)} MFMA hazards, e.g. {bad[:3]}"
 

@@ -303,8 +303,6 @@ def test_fp8_poisoned_unused_slots_are_never_read(mla, kind):
     assert_close(o2, l2, *ref(w))
 
 
-@pytest.mark.skip(reason="the fp8 cache still runs the older decode kernel, whose summation "
-                         "order differs from the bf16 tile kernel; bit identity needs one kernel")
 def test_fp8_equals_bf16_path_on_the_same_values(mla):
     """Every e4m3 value is a bf16 value: a bf16 cache holding dec(byte) * delta
     with delta a power of two gives bit-identical scores, so the outputs of
