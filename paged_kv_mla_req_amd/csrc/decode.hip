@@ -1041,6 +1041,11 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
   };
   park_offsets();
   load_q(cb);
+  // the first page and the queries land here, so that no path into the page
+  // loop below leaves query loads in flight (the compiler would otherwise
+  // wait for them at the score MFMAs of every page, behind the next page's
+  // loads issued there)
+  __builtin_amdgcn_s_waitcnt(0x0f70);
   while (true) {
     // ---- one piece: pages [cp, cend) of request cb ---------------------------
     const int32_t L = uniform_load(seq_lens, cb);
@@ -1057,8 +1062,15 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
       } while (ncb < b_last && page_count(uniform_load(seq_lens, ncb)) <= 0);
     }
     // on the piece's last page, if another piece follows: load its queries
+    // and wait for them at once (with the load in the same branch, no path
+    // back to the score MFMAs leaves query loads in flight; the compiler
+    // would otherwise wait for them at the score MFMAs of every page, behind
+    // the next page's loads issued there)
     auto prefetch_q = [&]() {
-      if (cp + 1 == cend && it + 1 < total && cb < b_last) load_q(ncb);
+      if (cp + 1 == cend && it + 1 < total && cb < b_last) {
+        load_q(ncb);
+        __builtin_amdgcn_s_waitcnt(0x0f70);
+      }
     };
     zero_acc(oacc);
     float m_run = -INFINITY, l_run = 0.f;
