@@ -314,6 +314,37 @@ mla_status mla_merge_states(const void* partial_o, const float* partial_lse,
                             hipStream_t stream);
 
 /*
+ * mla_decode_static — mla_decode and then mla_merge_states in one call that
+ * allocates nothing and takes no workspace: for callers that cannot allocate
+ * device memory or hand one in (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).
+ *
+ * Arguments and results are those of mla_decode without partial_o,
+ * partial_lse and partial_slots: every request's final o goes to out and its
+ * lse to lse (or nowhere if lse is NULL), whatever its number of pieces.
+ * The split pieces' partial states live in a device array of the library,
+ * MLA_STATIC_WORKSPACE_BYTES (64 MiB) per GPU, held from the first call on
+ * that GPU until the process ends; a call needs
+ * (bs + num_parts) * q_len * num_heads * 1028 bytes of it.
+ *
+ * Every call on one GPU uses that GPU's one array: calls that overlap on a
+ * GPU (on different streams, or from several host threads) race and must be
+ * ordered by the caller.  Nothing in the array needs to start at zero: each
+ * slot the merge reads is written by the decode of the same call.
+ *
+ * Errors: those of mla_decode and mla_merge_states; CAPACITY when the
+ * partial states would exceed MLA_STATIC_WORKSPACE_BYTES; DEVICE when the
+ * array's address cannot be found on the current device.
+ */
+#define MLA_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+mla_status mla_decode_static(const void* q, int32_t bs, int32_t q_len, int32_t num_heads,
+                             const void* kv_cache, int32_t kv_dtype, int64_t num_pages,
+                             const int32_t* block_table, int32_t bt_row_stride,
+                             const int32_t* seq_lens, const int32_t* tile_plan, int32_t num_parts,
+                             const int32_t* split_indptr, float softmax_scale, int32_t causal,
+                             const float* kv_descale, void* out, float* lse, hipStream_t stream);
+
+/*
  * mla_set_kv_buffer — store the new tokens' latent rows in the paged cache
  * (token_to_kv_pool.set_kv_buffer(layer, cache_loc, k, v) with
  * cache_loc = out_cache_loc, which forward_decode and the target-verify

@@ -273,6 +273,54 @@ def mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tenso
         partial_o.shape[0], _p(out), _p(lse), _stream(stream)))
 
 
+def mla_decode_static(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+                      seq_lens: torch.Tensor, tile_plan: torch.Tensor, split_indptr: torch.Tensor,
+                      softmax_scale: float, *, out: torch.Tensor,
+                      lse: Optional[torch.Tensor] = None, kv_dtype="bf16",
+                      kv_descale: Optional[torch.Tensor] = None, causal: bool = True,
+                      stream=None) -> None:
+    """Decode and merge with the library's own partial-state workspace
+    (mla_decode_static): allocates nothing, takes no workspace."""
+    _need(q, "q", (torch.bfloat16,), 4)
+    code = _kv_code(kv_dtype)
+    kv_ok = (torch.bfloat16, torch.int16, torch.uint16) if code == MLA_KV_BF16 else (
+        torch.uint8, torch.float8_e4m3fn)
+    _need(kv_cache, "kv_cache", kv_ok, 3)
+    if kv_cache.shape[1:] != (PAGE_SIZE, LATENT_DIM):
+        raise ValueError(f"kv_cache must be [pages, 64, 576], got {tuple(kv_cache.shape)}")
+    bs, q_len, heads, d = q.shape
+    if d != LATENT_DIM:
+        raise ValueError("q must be [bs, q_len, heads, 576]")
+    _need(block_table, "block_table", (torch.int32,), 2)
+    _need(seq_lens, "seq_lens", (torch.int32,), 1)
+    _need(tile_plan, "tile_plan", (torch.int32,), 2)
+    _need(split_indptr, "split_indptr", (torch.int32,), 1)
+    _need(out, "out", (torch.bfloat16,), 4)
+    _shape(out, "out", (bs, q_len, heads, V_DIM))
+    if lse is not None:
+        _need(lse, "lse", (torch.float32,), 3)
+        _shape(lse, "lse", (bs, q_len, heads))
+    if kv_descale is not None:
+        _need(kv_descale, "kv_descale", (torch.float32,))
+        if kv_descale.numel() < 1:
+            raise ValueError("kv_descale must hold one value")
+    if block_table.shape[0] < bs:
+        raise ValueError(f"block_table has {block_table.shape[0]} rows, needs {bs}")
+    _shape(seq_lens, "seq_lens", (bs,))
+    if split_indptr.shape[0] < bs + 1:
+        raise ValueError(f"split_indptr needs bs + 1 = {bs + 1} entries")
+    if tile_plan.shape[1] != 8:
+        raise ValueError("tile_plan must be [num_parts, 8]")
+    _same_device(("q", q), ("kv_cache", kv_cache), ("block_table", block_table),
+                 ("seq_lens", seq_lens), ("tile_plan", tile_plan), ("split_indptr", split_indptr),
+                 ("out", out), ("lse", lse), ("kv_descale", kv_descale))
+    _lib.check(_lib.lib().mla_decode_static(
+        _p(q), bs, q_len, heads, _p(kv_cache), code, kv_cache.shape[0], _p(block_table),
+        block_table.shape[1], _p(seq_lens), _p(tile_plan), tile_plan.shape[0], _p(split_indptr),
+        float(softmax_scale), 1 if causal else 0, _p(kv_descale), _p(out), _p(lse),
+        _stream(stream)))
+
+
 def time_next_decode(start: torch.cuda.Event, stop: torch.cuda.Event) -> None:
     """The next mla_decode on this thread records ``start``/``stop`` at its
     kernel's own begin and end (mla_decode_time_next_launch).  The events

@@ -47,6 +47,9 @@ SIGNATURES = {
     "mla_merge_states": (_c_i32, [_c_p, _c_p, _c_i32, _c_p, _c_i32, _c_i32, _c_i32, _c_p, _c_p,
                                   _c_p]),
     "mla_decode_time_next_launch": (_c_i32, [_c_p, _c_p]),
+    "mla_decode_static": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_p, _c_i32, _c_i64, _c_p,
+                                   _c_i32, _c_p, _c_p, _c_i32, _c_p, _c_f32, _c_i32, _c_p, _c_p,
+                                   _c_p, _c_p]),
     "mla_set_kv_buffer": (_c_i32, [_c_p, _c_i64, _c_p, _c_i32, _c_p, _c_i32, _c_i64, _c_p, _c_p]),
     "mla_quantize_q_fp8": (_c_i32, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
 }

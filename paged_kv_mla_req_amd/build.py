@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmla_decode.so")
-SOURCES = ["abi.hip", "block_table.hip", "plan.hip", "decode.hip", "merge.hip", "append.hip"]
+SOURCES = ["abi.hip", "block_table.hip", "plan.hip", "decode.hip", "merge.hip", "append.hip",
+           "noalloc.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms stay disabled: the compiler would otherwise emit

@@ -193,3 +193,19 @@ def test_quantize_q_argument_errors():
     assert f(FAKE, 576, 2**31, FAKE, FAKE, None) == _lib.MLA_ERR_UNSUPPORTED
     assert _lib.lib().mla_last_error_message().startswith(b"mla_quantize_q_fp8")
     assert f(None, 576, 0, FAKE, FAKE, None) == _lib.MLA_OK
+
+
+def test_decode_static_rejects_before_any_launch():
+    """mla_decode_static checks its sizes and its workspace limit on the host:
+    a call whose partial states exceed MLA_STATIC_WORKSPACE_BYTES comes back
+    CAPACITY without touching the device."""
+    f = _lib.lib().mla_decode_static
+    FAKE = ctypes.c_void_p(16)
+    args = lambda bs, q_len, heads, parts: (FAKE, bs, q_len, heads, FAKE, 0, 100, FAKE, 8, FAKE,
+                                           FAKE, parts, FAKE, 0.1, 1, None, FAKE, None, None)
+    assert f(*args(0, 1, 16, 1)) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert f(*args(2, 1, 16, 0)) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert f(*args(2, 1, 600, 1)) == _lib.MLA_ERR_UNSUPPORTED
+    # (512 + 256) slots * 128 rows * 1028 bytes = 101 MB > 64 MiB
+    assert f(*args(512, 1, 128, 256)) == _lib.MLA_ERR_CAPACITY
+    assert b"static workspace" in _lib.lib().mla_last_error_message()
