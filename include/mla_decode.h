@@ -274,6 +274,37 @@ mla_status mla_decode(const void* q, int32_t bs, int32_t q_len, int32_t num_head
                       int32_t partial_slots, void* out, float* lse, hipStream_t stream);
 
 /*
+ * mla_decode_q8 — mla_decode with an e4m3 query over an e4m3 cache (the fp8
+ * branch of forward_decode on the FlashMLA page: q quantised with
+ * scaled_fp8_quant, here mla_quantize_q_fp8, and handed to the kernel with
+ * descale_q and descale_k).
+ *
+ * Computes what mla_decode computes with the query row value
+ * q_r = e4m3fn(q_fp8 code) * (*q_descale) and the cache value
+ * e4m3fn(byte) * (*kv_descale).  The scores are sums of exact products of
+ * e4m3 codes (matrix cores, fp32 accumulation) times
+ * softmax_scale * q_descale * kv_descale; the weights and V enter the output
+ * contraction in bf16 (V exactly), accumulated in fp32, as in mla_decode.
+ *
+ *   q_fp8      uint8 e4m3fn codes [bs, q_len, num_heads, 576], contiguous,
+ *              16-byte aligned
+ *   q_descale  device fp32 scalar, finite (may be 0 or negative); read on
+ *              the device
+ *   kv_cache   [num_pages, 64, 576] e4m3fn bytes
+ *   the rest   as for mla_decode (kv_descale is required)
+ *
+ * Errors: those of mla_decode for an MLA_KV_FP8_E4M3 cache, and
+ * INVALID_ARGUMENT for a NULL q_descale.
+ */
+mla_status mla_decode_q8(const void* q_fp8, const float* q_descale, int32_t bs, int32_t q_len,
+                         int32_t num_heads, const void* kv_cache, int64_t num_pages,
+                         const int32_t* block_table, int32_t bt_row_stride,
+                         const int32_t* seq_lens, const int32_t* tile_plan, int32_t num_parts,
+                         const int32_t* split_indptr, float softmax_scale, int32_t causal,
+                         const float* kv_descale, void* partial_o, float* partial_lse,
+                         int32_t partial_slots, void* out, float* lse, hipStream_t stream);
+
+/*
  * mla_decode_time_next_launch — measurement hook.  The next mla_decode call
  * on this host thread launches its kernel with hipExtLaunchKernel so that
  * `start` and `stop` (events the caller created; either may be NULL) take

@@ -220,15 +220,11 @@ def partial_buffers(bs: int, rows_per_req: int, num_parts: int,
             torch.empty((slots, rows_per_req), dtype=torch.float32, device=device))
 
 
-def mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
-               seq_lens: torch.Tensor, tile_plan: torch.Tensor, split_indptr: torch.Tensor,
-               softmax_scale: float, *, partial_o: torch.Tensor, partial_lse: torch.Tensor,
-               out: torch.Tensor, lse: Optional[torch.Tensor] = None, kv_dtype="bf16",
-               kv_descale: Optional[torch.Tensor] = None, causal: bool = True,
-               stream=None) -> None:
-    """Split attention over the plan's pieces (mla_decode)."""
-    _need(q, "q", (torch.bfloat16,), 4)
-    code = _kv_code(kv_dtype)
+def _check_decode(q, q_dtypes, kv_cache, code, block_table, seq_lens, tile_plan, split_indptr,
+                  out, lse, kv_descale, partial_o=None, partial_lse=None, q_descale=None):
+    """Shape, dtype and device checks shared by the decode entry points;
+    returns (bs, q_len, heads)."""
+    _need(q, "q", q_dtypes, 4)
     kv_ok = (torch.bfloat16, torch.int16, torch.uint16) if code == MLA_KV_BF16 else (
         torch.uint8, torch.float8_e4m3fn)
     _need(kv_cache, "kv_cache", kv_ok, 3)
@@ -241,20 +237,22 @@ def mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tenso
     _need(seq_lens, "seq_lens", (torch.int32,), 1)
     _need(tile_plan, "tile_plan", (torch.int32,), 2)
     _need(split_indptr, "split_indptr", (torch.int32,), 1)
-    _need(partial_o, "partial_o", (torch.bfloat16,), 3)
-    _need(partial_lse, "partial_lse", (torch.float32,), 2)
     _need(out, "out", (torch.bfloat16,), 4)
+    _shape(out, "out", (bs, q_len, heads, V_DIM))
     if lse is not None:
         _need(lse, "lse", (torch.float32,), 3)
         _shape(lse, "lse", (bs, q_len, heads))
-    if kv_descale is not None:
-        _need(kv_descale, "kv_descale", (torch.float32,))
-        if kv_descale.numel() < 1:
-            raise ValueError("kv_descale must hold one value")
+    for name, t in (("kv_descale", kv_descale), ("q_descale", q_descale)):
+        if t is not None:
+            _need(t, name, (torch.float32,))
+            if t.numel() < 1:
+                raise ValueError(f"{name} must hold one value")
     rows = q_len * heads
-    _shape(out, "out", (bs, q_len, heads, V_DIM))
-    if partial_o.shape[1:] != (rows, V_DIM) or partial_lse.shape != (partial_o.shape[0], rows):
-        raise ValueError("partial buffers do not match q")
+    if partial_o is not None or partial_lse is not None:
+        _need(partial_o, "partial_o", (torch.bfloat16,), 3)
+        _need(partial_lse, "partial_lse", (torch.float32,), 2)
+        if partial_o.shape[1:] != (rows, V_DIM) or partial_lse.shape != (partial_o.shape[0], rows):
+            raise ValueError("partial buffers do not match q")
     if block_table.shape[0] < bs:
         raise ValueError(f"block_table has {block_table.shape[0]} rows, needs {bs}")
     _shape(seq_lens, "seq_lens", (bs,))
@@ -265,12 +263,47 @@ def mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tenso
     _same_device(("q", q), ("kv_cache", kv_cache), ("block_table", block_table),
                  ("seq_lens", seq_lens), ("tile_plan", tile_plan), ("split_indptr", split_indptr),
                  ("partial_o", partial_o), ("partial_lse", partial_lse), ("out", out),
-                 ("lse", lse), ("kv_descale", kv_descale))
+                 ("lse", lse), ("kv_descale", kv_descale), ("q_descale", q_descale))
+    return bs, q_len, heads
+
+
+def mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+               seq_lens: torch.Tensor, tile_plan: torch.Tensor, split_indptr: torch.Tensor,
+               softmax_scale: float, *, partial_o: torch.Tensor, partial_lse: torch.Tensor,
+               out: torch.Tensor, lse: Optional[torch.Tensor] = None, kv_dtype="bf16",
+               kv_descale: Optional[torch.Tensor] = None, causal: bool = True,
+               stream=None) -> None:
+    """Split attention over the plan's pieces (mla_decode)."""
+    code = _kv_code(kv_dtype)
+    bs, q_len, heads = _check_decode(q, (torch.bfloat16,), kv_cache, code, block_table, seq_lens,
+                                     tile_plan, split_indptr, out, lse, kv_descale, partial_o,
+                                     partial_lse)
     _lib.check(_lib.lib().mla_decode(
         _p(q), bs, q_len, heads, _p(kv_cache), code, kv_cache.shape[0], _p(block_table),
         block_table.shape[1], _p(seq_lens), _p(tile_plan), tile_plan.shape[0], _p(split_indptr),
         float(softmax_scale), 1 if causal else 0, _p(kv_descale), _p(partial_o), _p(partial_lse),
         partial_o.shape[0], _p(out), _p(lse), _stream(stream)))
+
+
+def mla_decode_q8(q_fp8: torch.Tensor, q_descale: torch.Tensor, kv_cache: torch.Tensor,
+                  block_table: torch.Tensor, seq_lens: torch.Tensor, tile_plan: torch.Tensor,
+                  split_indptr: torch.Tensor, softmax_scale: float, *, kv_descale: torch.Tensor,
+                  partial_o: torch.Tensor, partial_lse: torch.Tensor, out: torch.Tensor,
+                  lse: Optional[torch.Tensor] = None, causal: bool = True,
+                  stream=None) -> None:
+    """mla_decode with an e4m3 query (codes from quantize_q_fp8, value
+    code * q_descale) over an e4m3 cache (mla_decode_q8)."""
+    if q_descale is None or kv_descale is None:
+        raise ValueError("q_descale and kv_descale are required")
+    bs, q_len, heads = _check_decode(q_fp8, (torch.uint8, torch.float8_e4m3fn), kv_cache,
+                                     MLA_KV_FP8_E4M3, block_table, seq_lens, tile_plan,
+                                     split_indptr, out, lse, kv_descale, partial_o, partial_lse,
+                                     q_descale)
+    _lib.check(_lib.lib().mla_decode_q8(
+        _p(q_fp8), _p(q_descale), bs, q_len, heads, _p(kv_cache), kv_cache.shape[0],
+        _p(block_table), block_table.shape[1], _p(seq_lens), _p(tile_plan), tile_plan.shape[0],
+        _p(split_indptr), float(softmax_scale), 1 if causal else 0, _p(kv_descale),
+        _p(partial_o), _p(partial_lse), partial_o.shape[0], _p(out), _p(lse), _stream(stream)))
 
 
 def mla_decode_static(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
@@ -281,39 +314,9 @@ def mla_decode_static(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torc
                       stream=None) -> None:
     """Decode and merge with the library's own partial-state workspace
     (mla_decode_static): allocates nothing, takes no workspace."""
-    _need(q, "q", (torch.bfloat16,), 4)
     code = _kv_code(kv_dtype)
-    kv_ok = (torch.bfloat16, torch.int16, torch.uint16) if code == MLA_KV_BF16 else (
-        torch.uint8, torch.float8_e4m3fn)
-    _need(kv_cache, "kv_cache", kv_ok, 3)
-    if kv_cache.shape[1:] != (PAGE_SIZE, LATENT_DIM):
-        raise ValueError(f"kv_cache must be [pages, 64, 576], got {tuple(kv_cache.shape)}")
-    bs, q_len, heads, d = q.shape
-    if d != LATENT_DIM:
-        raise ValueError("q must be [bs, q_len, heads, 576]")
-    _need(block_table, "block_table", (torch.int32,), 2)
-    _need(seq_lens, "seq_lens", (torch.int32,), 1)
-    _need(tile_plan, "tile_plan", (torch.int32,), 2)
-    _need(split_indptr, "split_indptr", (torch.int32,), 1)
-    _need(out, "out", (torch.bfloat16,), 4)
-    _shape(out, "out", (bs, q_len, heads, V_DIM))
-    if lse is not None:
-        _need(lse, "lse", (torch.float32,), 3)
-        _shape(lse, "lse", (bs, q_len, heads))
-    if kv_descale is not None:
-        _need(kv_descale, "kv_descale", (torch.float32,))
-        if kv_descale.numel() < 1:
-            raise ValueError("kv_descale must hold one value")
-    if block_table.shape[0] < bs:
-        raise ValueError(f"block_table has {block_table.shape[0]} rows, needs {bs}")
-    _shape(seq_lens, "seq_lens", (bs,))
-    if split_indptr.shape[0] < bs + 1:
-        raise ValueError(f"split_indptr needs bs + 1 = {bs + 1} entries")
-    if tile_plan.shape[1] != 8:
-        raise ValueError("tile_plan must be [num_parts, 8]")
-    _same_device(("q", q), ("kv_cache", kv_cache), ("block_table", block_table),
-                 ("seq_lens", seq_lens), ("tile_plan", tile_plan), ("split_indptr", split_indptr),
-                 ("out", out), ("lse", lse), ("kv_descale", kv_descale))
+    bs, q_len, heads = _check_decode(q, (torch.bfloat16,), kv_cache, code, block_table, seq_lens,
+                                     tile_plan, split_indptr, out, lse, kv_descale)
     _lib.check(_lib.lib().mla_decode_static(
         _p(q), bs, q_len, heads, _p(kv_cache), code, kv_cache.shape[0], _p(block_table),
         block_table.shape[1], _p(seq_lens), _p(tile_plan), tile_plan.shape[0], _p(split_indptr),
@@ -362,10 +365,13 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
            kv_descale: Optional[torch.Tensor] = None, causal: bool = True,
            num_parts: Optional[int] = None, plan=None, workspace=None,
            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+           q_descale: Optional[torch.Tensor] = None,
            stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """mla_decode followed by mla_merge_states; returns (out bf16 [bs, q_len, H, 512],
-    lse fp32 [bs, q_len, H]).  ``plan`` = (tile_plan, split_indptr) from plan_splits,
-    ``workspace`` = (partial_o, partial_lse) from partial_buffers."""
+    """mla_decode (mla_decode_q8 for a uint8 / e4m3 query, which needs
+    ``q_descale`` and an fp8 cache) followed by mla_merge_states; returns
+    (out bf16 [bs, q_len, H, 512], lse fp32 [bs, q_len, H]).  ``plan`` =
+    (tile_plan, split_indptr) from plan_splits, ``workspace`` = (partial_o,
+    partial_lse) from partial_buffers."""
     bs, q_len, heads, _ = q.shape
     rows = q_len * heads
     if plan is None:
@@ -377,9 +383,16 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
         out = torch.empty((bs, q_len, heads, V_DIM), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((bs, q_len, heads), dtype=torch.float32, device=q.device)
-    mla_decode(q, kv_cache, block_table, seq_lens, tile_plan, split_indptr, softmax_scale,
-               partial_o=workspace[0], partial_lse=workspace[1], out=out, lse=lse,
-               kv_dtype=kv_dtype, kv_descale=kv_descale, causal=causal, stream=stream)
+    if q.dtype in (torch.uint8, torch.float8_e4m3fn):
+        if _kv_code(kv_dtype) != MLA_KV_FP8_E4M3:
+            raise ValueError("an e4m3 query needs kv_dtype='fp8_e4m3'")
+        mla_decode_q8(q, q_descale, kv_cache, block_table, seq_lens, tile_plan, split_indptr,
+                      softmax_scale, kv_descale=kv_descale, partial_o=workspace[0],
+                      partial_lse=workspace[1], out=out, lse=lse, causal=causal, stream=stream)
+    else:
+        mla_decode(q, kv_cache, block_table, seq_lens, tile_plan, split_indptr, softmax_scale,
+                   partial_o=workspace[0], partial_lse=workspace[1], out=out, lse=lse,
+                   kv_dtype=kv_dtype, kv_descale=kv_descale, causal=causal, stream=stream)
     merge_states(workspace[0], workspace[1], split_indptr, out, lse, stream=stream)
     return out, lse
 

@@ -44,6 +44,9 @@ SIGNATURES = {
     "mla_decode": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_p, _c_i32, _c_i64, _c_p, _c_i32,
                             _c_p, _c_p, _c_i32, _c_p, _c_f32, _c_i32, _c_p, _c_p, _c_p, _c_i32,
                             _c_p, _c_p, _c_p]),
+    "mla_decode_q8": (_c_i32, [_c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_p, _c_i64, _c_p, _c_i32,
+                               _c_p, _c_p, _c_i32, _c_p, _c_f32, _c_i32, _c_p, _c_p, _c_p,
+                               _c_i32, _c_p, _c_p, _c_p]),
     "mla_merge_states": (_c_i32, [_c_p, _c_p, _c_i32, _c_p, _c_i32, _c_i32, _c_i32, _c_p, _c_p,
                                   _c_p]),
     "mla_decode_time_next_launch": (_c_i32, [_c_p, _c_p]),

@@ -730,6 +730,221 @@ __device__ __forceinline__ void combined_chain(f32x16& sc, f32x16 (&oacc)[kVTile
   c_steps(sc, oacc, op, pop, qreg, a, va, hook, pay, std::make_integer_sequence<int, kCSlots>{});
 }
 
+// ---- fp8 query (e4m3 codes) over an e4m3 cache ------------------------------
+// The scores run on v_mfma_f32_32x32x64_f8f6f4 (both operands e4m3, 64
+// columns per MFMA: 9 per 32-key tile instead of 36), straight from the
+// page's e4m3 bytes in LDS; the output contraction stays bf16 (the weights p
+// keep bf16 precision; V comes from the exact e4m3 -> bf16 conversion).
+//
+// LDS for this variant: the bf16 V page (8 column blocks of 8 KiB, the
+// layout of the bf16 page above) at offset 0, and two e4m3 staging buffers
+// from kQ8Stage on.  A staging buffer is 9 column blocks of 4 KiB (64
+// columns of all 64 keys, 64 bytes per key); the 16-byte chunk c of key k in
+// a block sits at slot c ^ f8_swz(k), f8_swz(k) = bit2(k) + 2 bit4(k), so
+// that the score operand reads (32 keys, two chunks each) touch every bank
+// once per 16 lanes.
+//
+// V needs no pass of its own: every wave reads the whole page as score
+// operands anyway, so while its score MFMAs run wave w converts the operand
+// registers of column blocks 2w and 2w + 1 (both key tiles) to bf16 and
+// writes them to the V page; one barrier (LDS only) between the score and
+// the output phase publishes them.
+constexpr int kKSteps8 = kD / 64;            // 9 fp8 k-steps of 64 columns
+constexpr int kQ8Stage = kDv * kPage * 2;    // 65536: staging buffers after the V page
+constexpr int kK8Ahead = 3;                  // operand reads run 3 MFMAs ahead
+constexpr int kK8Ring = kK8Ahead + 1;
+static_assert(kQ8Stage + 2 * kPageBytesF8 <= 2 * kPageBytes, "q8 LDS layout fits the page buffers");
+
+typedef uint32_t u32x8 __attribute__((__vector_size__(8 * sizeof(uint32_t))));
+
+__device__ __forceinline__ int f8_swz(int k) { return ((k >> 2) & 1) + 2 * ((k >> 4) & 1); }
+
+// Load K of wave w (K < 9) of an e4m3 page into the staging layout above:
+// column block K, keys 16w .. 16w + 15; lane i writes slot i % 4 of key
+// 16w + i / 4 from global chunk (i % 4) ^ f8_swz(key) (voff, per lane; the
+// column block is the immediate offset, which moves the LDS destination
+// too).
+template <int K>
+__device__ __forceinline__ void issue_one_load_q8(__amdgpu_buffer_rsrc_t rsrc, uint8_t* stage,
+                                                  int wave, uint32_t voff) {
+  constexpr int imm = 64 * K;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rsrc, LDS_PTR(void, stage + 4096 * K + 1024 * wave - imm), 16, voff, 0, imm, kStreamLoad);
+}
+
+template <int... K>
+__device__ __forceinline__ void issue_loads_q8(std::integer_sequence<int, K...>,
+                                               __amdgpu_buffer_rsrc_t rsrc, uint8_t* stage,
+                                               int wave, uint32_t voff) {
+  (issue_one_load_q8<K>(rsrc, stage, wave, voff), ...);
+}
+
+__device__ __forceinline__ uint32_t q8_load_offset(uint32_t lane, int wave) {
+  const int key = 16 * wave + (int)(lane >> 2);
+  return key * kD + 16 * (((int)lane & 3) ^ f8_swz(key));
+}
+
+// Per-lane LDS offsets of the q8 page loop (lane (m, h), m = lane % 32):
+//  k: score A operand, key sigma(m) (as in lane_offsets), chunk 2h of the
+//     column block; chunk 2h + 1 is at k ^ 16;
+//  d: V conversion, bf16 chunk 4h of key sigma(m) in its column block;
+//     chunks 4h + i are at d ^ 16 i.
+struct Q8Offsets {
+  uint32_t k, d;
+};
+__device__ __forceinline__ Q8Offsets q8_offsets(uint32_t lane) {
+  const int n = lane & 31, h = lane >> 5;
+  const int sig = 16 * ((n >> 2) & 1) + 4 * (n >> 3) + (n & 3);
+  Q8Offsets o;
+  o.k = sig * 64 + (((2 * h) ^ f8_swz(sig)) << 4);
+  o.d = sig * 128 + (((4 * h) ^ chunk_swz(sig)) << 4);
+  return o;
+}
+
+template <bool FIRST>
+__device__ __forceinline__ void mfma_s8(f32x16& c, const u32x8& a, const u32x8& b) {
+  if constexpr (FIRST)
+    asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+
+struct K8 {
+  u32x4 lo, hi;  // columns 32h .. 32h + 15 and 32h + 16 .. 32h + 31 of the block
+};
+
+// Score operand of step S (tile S / 9, column block S % 9): two 16-byte reads.
+template <int S>
+__device__ __forceinline__ void k8_read(K8& dst, uint32_t a0, uint32_t a1) {
+  constexpr int OFF = 4096 * (S % kKSteps8) + 2048 * (S / kKSteps8);
+  asm volatile("ds_read_b128 %0, %2 offset:%4\n\tds_read_b128 %1, %3 offset:%4"
+               : "=&v"(dst.lo), "=&v"(dst.hi)
+               : "v"(a0), "v"(a1), "i"(OFF));
+}
+
+template <bool HI>
+__device__ __forceinline__ uint32_t cvt_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+// the four e4m3 values of w to bf16
+__device__ __forceinline__ uint2 cvt_bf16x4(uint32_t w) {
+  return make_uint2(cvt_bf16x2<false>(w), cvt_bf16x2<true>(w));
+}
+// 8 e4m3 values (words w0, w1) to one 16-byte chunk of bf16
+__device__ __forceinline__ u32x4 cvt_chunk(uint32_t w0, uint32_t w1) {
+  const uint2 a = cvt_bf16x4(w0), b = cvt_bf16x4(w1);
+  return (u32x4){a.x, a.y, b.x, b.y};
+}
+
+// The 32 e4m3 values of operand r (step S: key tile S / 9, column block
+// S % 9) to bf16, written to the V page as the lane's 4 chunks.  Exact.
+template <int S>
+__device__ __forceinline__ void k8_convert(const K8& r, const uint32_t (&d)[4]) {
+  constexpr int OFF = 8192 * (S % kKSteps8) + 4096 * (S / kKSteps8);
+  const u32x4 c0 = cvt_chunk(r.lo[0], r.lo[1]), c1 = cvt_chunk(r.lo[2], r.lo[3]);
+  const u32x4 c2 = cvt_chunk(r.hi[0], r.hi[1]), c3 = cvt_chunk(r.hi[2], r.hi[3]);
+  asm volatile(
+      "ds_write_b128 %0, %4 offset:%8\n\t"
+      "ds_write_b128 %1, %5 offset:%8\n\t"
+      "ds_write_b128 %2, %6 offset:%8\n\t"
+      "ds_write_b128 %3, %7 offset:%8" ::"v"(d[0]),
+      "v"(d[1]), "v"(d[2]), "v"(d[3]), "v"(c0), "v"(c1), "v"(c2), "v"(c3), "i"(OFF));
+}
+
+// Step S of the 18-step score chain (tiles 0 and 1 back to back): MFMA S,
+// pay(ic<S>), wave `conv`'s conversion of its column blocks, the operand read
+// for S + kK8Ahead, the wait for S + 1 (the conversion writes, which also
+// count, only make it wait a little longer), hook(ic<S>).
+template <int S, typename Hook, typename Pay>
+__device__ __forceinline__ void s8_step(f32x16& sc0, f32x16& sc1, K8 (&ring)[kK8Ring],
+                                        const u32x8 (&qreg)[kKSteps8], uint32_t a0, uint32_t a1,
+                                        const uint32_t (&d)[4], int conv, Hook& hook, Pay& pay) {
+  constexpr int ks = S % kKSteps8, N = 2 * kKSteps8;
+  const K8& r = ring[S % kK8Ring];
+  const u32x8 a = __builtin_shufflevector(r.lo, r.hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  if constexpr (S < kKSteps8)
+    mfma_s8<ks == 0>(sc0, a, qreg[ks]);
+  else
+    mfma_s8<ks == 0>(sc1, a, qreg[ks]);
+  MLA_SB();
+  pay(ic<S>{});
+  MLA_SB();
+  if constexpr (ks < kDv / 64) {
+    if (conv == ks / 2) k8_convert<S>(r, d);
+  }
+  MLA_SB();
+  if constexpr (S + kK8Ahead < N) k8_read<S + kK8Ahead>(ring[(S + kK8Ahead) % kK8Ring], a0, a1);
+  MLA_SB();
+  if constexpr (S + 1 == N) {
+    mfma_tail();
+  } else {
+    constexpr int last = (S + kK8Ahead < N) ? S + kK8Ahead : N - 1;
+    lgkm_wait<2 * (last - (S + 1))>();
+  }
+  MLA_SB();
+  hook(ic<S>{});
+  MLA_SB();
+}
+
+template <typename Hook, typename Pay, int... S>
+__device__ __forceinline__ void s8_steps(f32x16& sc0, f32x16& sc1, K8 (&ring)[kK8Ring],
+                                         const u32x8 (&qreg)[kKSteps8], uint32_t a0, uint32_t a1,
+                                         const uint32_t (&d)[4], int conv, Hook& hook, Pay& pay,
+                                         std::integer_sequence<int, S...>) {
+  (s8_step<S>(sc0, sc1, ring, qreg, a0, a1, d, conv, hook, pay), ...);
+}
+
+template <int... S>
+__device__ __forceinline__ void s8_prologue(K8 (&ring)[kK8Ring], uint32_t a0, uint32_t a1,
+                                            std::integer_sequence<int, S...>) {
+  (k8_read<S>(ring[S], a0, a1), ...);
+}
+
+// S^T of both key tiles of a page (sc0: keys 0..31, sc1: keys 32..63), 18
+// MFMAs.  ka = LDS address of the lane's score operand in the page's
+// staging buffer (see q8_offsets), d = its conversion addresses in the V
+// page, conv = the wave's pair of column blocks.
+template <typename Hook, typename Pay>
+__device__ __forceinline__ void score_chain_q8(f32x16& sc0, f32x16& sc1,
+                                               const u32x8 (&qreg)[kKSteps8], uint32_t ka,
+                                               const uint32_t (&d)[4], int conv, Hook&& hook,
+                                               Pay&& pay) {
+  const uint32_t a1 = ka ^ 16u;
+  K8 ring[kK8Ring];
+  s8_prologue(ring, ka, a1, std::make_integer_sequence<int, kK8Ahead>{});
+  lgkm_wait<2 * (kK8Ahead - 1)>();
+  MLA_SB();
+  s8_steps(sc0, sc1, ring, qreg, ka, a1, d, conv, hook, pay,
+           std::make_integer_sequence<int, 2 * kKSteps8>{});
+}
+
+// Conversion share of a wave with no query rows (plain code): column blocks
+// 2w and 2w + 1, all 64 keys, lane = key.
+__device__ __forceinline__ void convert_share_q8(const uint8_t* stage, uint8_t* vpage, int wave) {
+  const int key = (int)lane_id();
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int blk = 2 * wave + b;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + 4096 * blk + 64 * key +
+                                                      16 * (c ^ f8_swz(key)));
+      const u32x4 lo = cvt_chunk(v[0], v[1]), hi = cvt_chunk(v[2], v[3]);
+      uint8_t* row = vpage + 8192 * blk + 128 * key;
+      *reinterpret_cast<u32x4*>(row + 16 * ((2 * c) ^ chunk_swz(key))) = lo;
+      *reinterpret_cast<u32x4*>(row + 16 * ((2 * c + 1) ^ chunk_swz(key))) = hi;
+    }
+  }
+}
+
+// Barrier for LDS data only: this wave's LDS operations are complete, then
+// every wave meets.  (__syncthreads also waits for the wave's global loads,
+// the next page's among them.)
+__device__ __forceinline__ void lds_barrier() {
+  lgkm_wait<0>();
+  __builtin_amdgcn_s_barrier();
+}
+
 // Element placed in payload slot 8 + d when 16 elements are spread over 27
 // slots (element i at 8 + 7i/4), or -1.
 __host__ __device__ constexpr int spread_slot_elem(int d) {
@@ -880,16 +1095,19 @@ __device__ __forceinline__ void store_rows(const f32x16 (&oacc)[kVTiles], float 
 }
 
 // FP8: the cache holds e4m3 bytes (kv_descale is read); else bf16.
-template <bool FP8>
+// Q8 (with FP8): q holds e4m3 codes whose value is code * q_descale[0].
+template <bool FP8, bool Q8>
 __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
                   const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
                   const int32_t* __restrict__ tile_plan, const int32_t* __restrict__ split_indptr,
-                  const float* __restrict__ kv_descale, uint16_t* __restrict__ partial_o,
-                  float* __restrict__ partial_lse, uint16_t* __restrict__ out,
-                  float* __restrict__ lse_out, DecodeParams P) {
+                  const float* __restrict__ kv_descale, const float* __restrict__ q_descale,
+                  uint16_t* __restrict__ partial_o, float* __restrict__ partial_lse,
+                  uint16_t* __restrict__ out, float* __restrict__ lse_out, DecodeParams P) {
+  static_assert(FP8 || !Q8, "an e4m3 query goes with an e4m3 cache");
   // bf16: two compute buffers.  fp8: compute buffer 0, and two e4m3 staging
-  // buffers in the space of compute buffer 1.
+  // buffers in the space of compute buffer 1.  fp8 query: the bf16 V page and
+  // two staging buffers (see kQ8Stage).
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kPageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t stage_all[kWaves][kStageBytes];
   constexpr int kSrcPageBytes = FP8 ? kPageBytesF8 : kPageBytes;
@@ -928,16 +1146,23 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
   int nlen = uniform_load(seq_lens, nb);
   int nend = (nb == b_last) ? pg_last : page_count(nlen);
   auto raw_of = [&](int b, int p) -> int32_t {
-    return p < P.bt_stride ? block_table[(int64_t)b * P.bt_stride + p] : 0;
+    return p < P.bt_stride ? block_table[(int64_t)b * P.bt_stride + p] : -1;
   };
   int32_t nraw = raw_of(nb, np);
-  // the cursor's physical page; entries outside the pool read page 0
-  auto nphys = [&]() -> int64_t { return (nraw >= 0 && nraw < P.num_pages) ? nraw : 0; };
+  // A block-table entry outside the pool (or a page past the table's width)
+  // is a caller error: the page is not read (its loads get an empty range,
+  // based at page 0) and every key of it is masked, so it contributes nothing.
+  auto cursor_bad = [&]() -> uint32_t { return (nraw >= 0 && nraw < P.num_pages) ? 0u : 1u; };
+  auto nphys = [&]() -> int64_t { return cursor_bad() ? 0 : nraw; };
   int nrows = min(kPage, max(0, nlen - np * kPage));
   // Loads of the cursor's page into LDS for page index `j` of the part.
   auto issue = [&](int j) {
-    const int vr = __builtin_amdgcn_readfirstlane(nrows);
-    if constexpr (FP8)
+    const int vr = __builtin_amdgcn_readfirstlane(cursor_bad() ? 0 : nrows);
+    if constexpr (Q8)
+      issue_loads_q8(std::make_integer_sequence<int, kKSteps8>{},
+                     page_rsrc<kD>(kv + nphys() * kSrcPageBytes, vr),
+                     smem + kQ8Stage + (j & 1) * kPageBytesF8, wave, q8_load_offset(lane, wave));
+    else if constexpr (FP8)
       issue_loads_f8(std::make_integer_sequence<int, kLoadsPerWaveF8>{},
                      page_rsrc<kD>(kv + nphys() * kSrcPageBytes, vr),
                      smem + kPageBytes + (j & 1) * kPageBytesF8, wave, wave * 1024 + 16 * lane);
@@ -962,6 +1187,9 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
   };
 
   issue(0);
+  // bit 0: the page computed next is a bad one (see cursor_bad); bit 1: the
+  // page after it
+  uint32_t badq = cursor_bad();
   advance();
 
   // Every wave passes exactly `total` barriers, one per page, whatever the
@@ -976,7 +1204,10 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
         issue(it + 1);
         advance();
       }
-      if constexpr (FP8) {
+      if constexpr (Q8) {
+        convert_share_q8(smem + kQ8Stage + (it & 1) * kPageBytesF8, smem, wave);
+        lds_barrier();
+      } else if constexpr (FP8) {
         convert_f8_page(smem + kPageBytes + (it & 1) * kPageBytesF8, smem, wave);
         __syncthreads();
       }
@@ -988,24 +1219,32 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
   // it.  It is worked out (and the cursor moved on, which starts the read of
   // the block-table entry after it) one page ahead, among the last output
   // MFMAs of a page, where the wave has issue slots to spare.
+  // Returns whether the cursor's page is a bad one.
   __amdgpu_buffer_rsrc_t next_rsrc;
-  auto next_range = [&](bool has) {
+  auto next_range = [&](bool has) -> uint32_t {
+    const uint32_t bad = has ? cursor_bad() : 0u;
     next_rsrc = page_rsrc<FP8 ? kD : kRowBytes>(
-        kv + nphys() * kSrcPageBytes, has ? __builtin_amdgcn_readfirstlane(nrows) : 0);
+        kv + nphys() * kSrcPageBytes,
+        (has && !bad) ? __builtin_amdgcn_readfirstlane(nrows) : 0);
+    return bad;
   };
-  next_range(1 < total);
+  badq |= next_range(1 < total) << 1;
   if (1 < total) advance();
 
   // Per-tensor dequantisation scale: scores use |delta| in the softmax scale
   // and the sign on q; the output is multiplied by delta.
+  // An e4m3 query multiplies the scores by q_descale as well.
   const float delta = FP8 ? kv_descale[0] : 1.0f;
+  const float qk_descale = Q8 ? delta * q_descale[0] : delta;
   // (kept above 0 so that a masked score, -inf, scales to -inf and never to
   // 0 * inf; a zero scale then weights the visible keys equally, to within
   // 1e-30 of a relative error)
-  const float c_log2 = fmaxf(P.scale_log2 * fabsf(delta), 1e-30f);
-  const uint32_t q_sign = (FP8 && delta < 0.f) ? 0x80008000u : 0u;
+  const float c_log2 = fmaxf(P.scale_log2 * fabsf(qk_descale), 1e-30f);
+  const uint32_t q_sign =
+      (FP8 && qk_descale < 0.f) ? (Q8 ? 0x80808080u : 0x80008000u) : 0u;
 
-  bf16x8 qreg[kKSteps];
+  // bf16 query: 36 k-steps of 8 values per lane; e4m3: 9 k-steps of 32.
+  std::conditional_t<Q8, u32x8[kKSteps8], bf16x8[kKSteps]> qreg;
   f32x16 oacc[kVTiles];
   // Query rows of request b into qreg.  A lane whose row is past the last one
   // reads row 0 instead: its results stay in that lane's row of the
@@ -1014,13 +1253,27 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
   auto load_q = [&](int b) {
     const uint32_t ql = pinned_lane();
     const int r = row0 + (int)(ql & 31);
-    const uint16_t* qrow =
-        q + ((int64_t)b * P.rows + (r < P.rows ? r : 0)) * kD + 8 * (int)(ql >> 5);
+    if constexpr (Q8) {
+      // lane (n, h): columns 64 ks + 32 h .. +31 of its row, the bytes the
+      // score operand holds for the same lane
+      const uint8_t* qrow = reinterpret_cast<const uint8_t*>(q) +
+                            ((int64_t)b * P.rows + (r < P.rows ? r : 0)) * kD +
+                            32 * (int)(ql >> 5);
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 16 * ks);
-      if (FP8) v ^= q_sign;
-      qreg[ks] = __builtin_bit_cast(bf16x8, v);
+      for (int ks = 0; ks < kKSteps8; ++ks) {
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(qrow + 64 * ks) ^ q_sign;
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(qrow + 64 * ks + 16) ^ q_sign;
+        qreg[ks] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    } else {
+      const uint16_t* qrow =
+          q + ((int64_t)b * P.rows + (r < P.rows ? r : 0)) * kD + 8 * (int)(ql >> 5);
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks) {
+        u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 16 * ks);
+        if (FP8) v ^= q_sign;
+        qreg[ks] = __builtin_bit_cast(bf16x8, v);
+      }
     }
   };
   int it = 0;  // pages of this part processed so far (selects the LDS buffer)
@@ -1034,10 +1287,13 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
   bool first_wait = true;
   // Lane offsets and lane id into the first KiB of the wave's staging area
   // (again after each piece's output, which uses that area).
+  // (fp8 query: the score operand and load offsets of its own layout)
   auto park_offsets = [&]() {
     const uint32_t pl = pinned_lane();
     const LaneOffsets o = lane_offsets(pl, wave);
-    *reinterpret_cast<u32x4*>(stage_all[wave] + 16 * pl) = (u32x4){o.k, o.v, o.load, pl};
+    const uint32_t ok = Q8 ? q8_offsets(pl).k : o.k;
+    const uint32_t ol = Q8 ? q8_load_offset(pl, wave) : o.load;
+    *reinterpret_cast<u32x4*>(stage_all[wave] + 16 * pl) = (u32x4){ok, o.v, ol, pl};
   };
   park_offsets();
   load_q(cb);
@@ -1093,33 +1349,43 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
       __syncthreads();
       const uint32_t plane = lov[3];
       const LaneOffsets lo = {lov[0], lov[1], lov[2]};
-      const lds_u8* base = LDS_PTR(uint8_t, smem) + (FP8 ? 0 : (it & 1) * kPageBytes);
+      const bool bad = badq & 1u;  // uniform: this page is a bad one, mask all its keys
+      // the page's LDS buffer: the compute page (fp8 query: the e4m3 staging
+      // buffer, which the score operands are read from)
+      const lds_u8* base =
+          LDS_PTR(uint8_t, smem) +
+          (Q8 ? kQ8Stage + (it & 1) * kPageBytesF8 : FP8 ? 0 : (it & 1) * kPageBytes);
       // The next page's loads are spread over the MFMA work (issued back to
       // back they would stall the wave until the address unit drains them).
       // Their range (next_rsrc) was worked out on the previous page.  After the
       // part's last page the loads still go out, over an empty range: they
       // only write zeros into the free buffer (and cost no branch per load);
       // the kernel waits for them before it ends.
-      uint8_t* const next_buf = FP8 ? smem + kPageBytes + ((it + 1) & 1) * kPageBytesF8
-                                    : smem + ((it + 1) & 1) * kPageBytes;
+      uint8_t* const next_buf = Q8    ? smem + kQ8Stage + ((it + 1) & 1) * kPageBytesF8
+                                : FP8 ? smem + kPageBytes + ((it + 1) & 1) * kPageBytesF8
+                                      : smem + ((it + 1) & 1) * kPageBytes;
       // load K of this wave's share, K < 18 (bf16) or K < 9 (e4m3)
       auto load = [&](auto kc) {
         constexpr int K = decltype(kc)::value;
-        if constexpr (FP8)
+        if constexpr (Q8)
+          issue_one_load_q8<K>(next_rsrc, next_buf, wave, lo.load);
+        else if constexpr (FP8)
           issue_one_load_f8<K>(next_rsrc, next_buf, wave, wave * 1024 + 16 * plane);
         else
           issue_one_load<K>(next_rsrc, next_buf, wave, lo.load, lo.load + 4 * (8 * kRowBytes));
       };
       auto hook_s0 = [&](auto g) { load(g); };
       auto no_hook = [](auto) {};
-      if constexpr (FP8) {
+      if constexpr (FP8 && !Q8) {
         convert_f8_page(smem + kPageBytes + (it & 1) * kPageBytesF8, smem, wave);
         __syncthreads();  // the compute page is complete
       }
 
-      // LDS byte addresses of this page's operands
+      // LDS byte addresses of this page's operands (fp8 query: V from the
+      // bf16 V page at the start of the LDS buffers)
       const uint32_t pbase = (uint32_t)(uintptr_t)base;
-      const uint32_t ka = pbase + lo.k, va = pbase + lo.v;
+      const uint32_t vbase = Q8 ? (uint32_t)(uintptr_t)LDS_PTR(uint8_t, smem) : pbase;
+      const uint32_t ka = pbase + lo.k, va = vbase + lo.v;
 
       {
         // The softmax of each tile runs in the shadow of the matrix work:
@@ -1138,14 +1404,23 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
           const int r = row0 + (int)(plane & 31);
           const int i_tok = r < P.rows ? r / P.heads : 0;
           const int32_t lim = P.causal ? L - P.q_len + i_tok : L - 1;  // last visible key
-          vis0 = lim - (cp * kPage + 16 * (int)(plane >> 5)) + 1;
+          vis0 = bad ? 0 : lim - (cp * kPage + 16 * (int)(plane >> 5)) + 1;
           vis1 = vis0 - 32;
         }
         auto mask_tile = [&](f32x16& sc, int vis) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) sc[i] = i < vis ? sc[i] : -INFINITY;
         };
-        score_tile<0>(sc0, ka, qreg, hook_s0, NoSlot{});
+        // the masking of tile sc: by vis on a MASKED page; on another page
+        // only if the page is a bad one (a uniform branch)
+        auto mask = [&](f32x16& sc, int vis) {
+          if constexpr (MASKED) {
+            mask_tile(sc, vis);
+          } else if (bad) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sc[i] = -INFINITY;
+          }
+        };
 
         float mx[4], ls[4];
         float m_tile = 0.f, neg_m = 0.f;
@@ -1197,70 +1472,6 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
           neg_m = m_run == -INFINITY ? 0.f : -m_run;  // -inf: no visible key yet
         };
         bf16x8 pop[2];
-        // payload slots of the combined chain
-        constexpr int kE0 = 5;                 // tile 0, keys 0..7: slots 5..8
-        constexpr int kE1 = kCPrefix + 1;      // tile 0, keys 8..15: slots 10, 16, 22, 28
-        constexpr int kLd = kCPrefix + 2;      // bf16 loads 9..17: slots 11, 14, .., 35
-        constexpr int kM1 = kCLastScore + 1;   // max(1): slots 59..63
-        constexpr int kW1 = kM1 + 5;           // tile 1, keys 0..7: slots 64..67
-        static_assert(kE0 + 4 == kCPrefix && kCPrefix == kCFirstOut && kE1 + 6 * 3 < kCOutU1 &&
-                          kW1 + 4 == kCSlots,
-                      "combined chain payload layout");
-        auto pay_c = [&](auto slot) {
-          constexpr int k = decltype(slot)::value;
-          if constexpr (k < kE0) {
-            if constexpr (MASKED && k == 0) mask_tile(sc0, vis0);
-            max_part(sc0, slot);
-          } else if constexpr (k < kE0 + 4) {
-            weight2(sc0, ic<2 * (k - kE0)>{});
-            if constexpr (k == kE0 + 3)
-              pop[0] = __builtin_bit_cast(bf16x8, (u32x4){pk[0], pk[1], pk[2], pk[3]});
-          } else if constexpr (k >= kE1 && k <= kE1 + 6 * 3 && (k - kE1) % 6 == 0) {
-            weight2(sc0, ic<8 + 2 * ((k - kE1) / 6)>{});
-            if constexpr (k == kE1 + 6 * 3) {
-              pop[1] = __builtin_bit_cast(bf16x8, (u32x4){pk[4], pk[5], pk[6], pk[7]});
-              fold_ls();
-            }
-          } else if constexpr (k >= kM1 && k < kM1 + 5) {
-            // the last score MFMA went out one slot before: let its result land
-            if constexpr (k == kM1) {
-              asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
-              MLA_SB();  // (reads of sc1 stay below the wait states)
-              if constexpr (MASKED) mask_tile(sc1, vis1);
-            }
-            max_part(sc1, ic<k - kM1>{});
-          } else if constexpr (k >= kW1) {
-            weight2(sc1, ic<2 * (k - kW1)>{});
-          }
-        };
-        auto hook_c = [&](auto slot) {
-          constexpr int k = decltype(slot)::value;
-          if constexpr (k == kE0 - 1) {
-            need = m_tile > m_run + kTau;
-            if (__any(need)) rescale();
-            neg_m = m_run == -INFINITY ? 0.f : -m_run;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) ls[j] = 0.f;
-          } else if constexpr (k == kW1 - 1) {
-            need = m_tile > m_run + kTau;
-          } else if constexpr (!FP8 && k >= kLd && k <= kLd + 3 * 8 && (k - kLd) % 3 == 0) {
-            load(ic<9 + (k - kLd) / 3>{});
-          }
-        };
-        combined_chain(sc1, oacc, pop, qreg, ka, va, hook_c, pay_c);
-        prefetch_q();
-        if (__any(need)) {
-          // the running max moves for tile 1: rescale (the chain has drained)
-          // and redo the weights of keys 0..7 under the new max
-          rescale();
-#pragma unroll
-          for (int j = 0; j < 4; ++j) ls[j] = 0.f;
-          weight2(sc1, ic<0>{});
-          weight2(sc1, ic<2>{});
-          weight2(sc1, ic<4>{});
-          weight2(sc1, ic<6>{});
-        }
-        pop[0] = __builtin_bit_cast(bf16x8, (u32x4){pk[0], pk[1], pk[2], pk[3]});
         // weights of keys 16..31 in slots 1, 5, 9, 13 (used from MFMA 16 on)
         auto pay_pv1 = [&](auto slot) {
           constexpr int k = decltype(slot)::value;
@@ -1271,12 +1482,145 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
           } else if constexpr (k == 14) {
             fold_ls();
           } else if constexpr (k == 17) {
-            next_range(it + 2 < total);  // page it + 2, loaded during page it + 1
+            // page it + 2, loaded during page it + 1
+            badq = (badq >> 1) | (next_range(it + 2 < total) << 1);
           } else if constexpr (k == 21) {
             if (it + 2 < total) advance();
           }
         };
-        pv_tile<1>(oacc, pop, va, no_hook, pay_pv1);
+        // the running max moves for tile 1 (the output chain of tile 0 has
+        // drained): rescale, and redo the weights of keys 0..7 under the new max
+        auto redo_tile1 = [&]() {
+          if (__any(need)) {
+            rescale();
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ls[j] = 0.f;
+            weight2(sc1, ic<0>{});
+            weight2(sc1, ic<2>{});
+            weight2(sc1, ic<4>{});
+            weight2(sc1, ic<6>{});
+          }
+          pop[0] = __builtin_bit_cast(bf16x8, (u32x4){pk[0], pk[1], pk[2], pk[3]});
+        };
+        if constexpr (Q8) {
+          // fp8 query:
+          //   S(0), S(1) as one chain of 18 | the next page's loads (steps 0..8),
+          //     this wave's V conversion, max(0), rescale decision, P(0) keys 0..7
+          //   barrier: every wave's share of the V page is written
+          //   PV(0) | P(0) keys 8..15, max(1), P(1) keys 0..7 under the running max
+          //   (rare: the running max moves for tile 1 -> rescale, redo those weights)
+          //   PV(1) | P(1) keys 8..15
+          const uint32_t d0 = vbase + q8_offsets(plane).d;
+          const uint32_t dq[4] = {d0, d0 ^ 16u, d0 ^ 32u, d0 ^ 48u};
+          auto hook_s8 = [&](auto step) {
+            constexpr int k = decltype(step)::value;
+            if constexpr (k < kKSteps8) {
+              load(step);
+            } else if constexpr (k == kKSteps8 + 4) {
+              need = m_tile > m_run + kTau;
+              if (__any(need)) rescale();
+              neg_m = m_run == -INFINITY ? 0.f : -m_run;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) ls[j] = 0.f;
+            }
+          };
+          auto pay_s8 = [&](auto step) {
+            constexpr int k = decltype(step)::value - kKSteps8;  // step of tile 1
+            if constexpr (k == 0) {
+              // the last MFMA of tile 0 went out one step before: let it land
+              asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+              MLA_SB();  // (reads of sc0 stay below the wait states)
+              mask(sc0, vis0);
+            }
+            if constexpr (k >= 0 && k < 5) {
+              max_part(sc0, ic<k>{});
+            } else if constexpr (k >= 5) {
+              weight2(sc0, ic<2 * (k - 5)>{});
+              if constexpr (k == 8)
+                pop[0] = __builtin_bit_cast(bf16x8, (u32x4){pk[0], pk[1], pk[2], pk[3]});
+            }
+          };
+          score_chain_q8(sc0, sc1, qreg, ka, dq, wave, hook_s8, pay_s8);
+          prefetch_q();
+          lds_barrier();
+          auto pay_pv0 = [&](auto slot) {
+            constexpr int k = decltype(slot)::value;
+            if constexpr (k < 8 && k % 2 == 1) {
+              weight2(sc0, ic<k + 7>{});  // elements 8, 10, 12, 14
+              if constexpr (k == 7)
+                pop[1] = __builtin_bit_cast(bf16x8, (u32x4){pk[4], pk[5], pk[6], pk[7]});
+            } else if constexpr (k == 8) {
+              fold_ls();
+            } else if constexpr (k >= 10 && k < 15) {
+              if constexpr (k == 10) mask(sc1, vis1);
+              max_part(sc1, ic<k - 10>{});
+            } else if constexpr (k >= 16 && k < 24 && k % 2 == 0) {
+              weight2(sc1, ic<k - 16>{});
+            }
+          };
+          auto hook_pv0 = [&](auto group) {
+            if constexpr (decltype(group)::value == 3) need = m_tile > m_run + kTau;
+          };
+          pv_tile<0>(oacc, pop, va, hook_pv0, pay_pv0);
+          redo_tile1();
+          pv_tile<1>(oacc, pop, va, no_hook, pay_pv1);
+        } else {
+          score_tile<0>(sc0, ka, qreg, hook_s0, NoSlot{});
+          // payload slots of the combined chain
+          constexpr int kE0 = 5;                 // tile 0, keys 0..7: slots 5..8
+          constexpr int kE1 = kCPrefix + 1;      // tile 0, keys 8..15: slots 10, 16, 22, 28
+          constexpr int kLd = kCPrefix + 2;      // bf16 loads 9..17: slots 11, 14, .., 35
+          constexpr int kM1 = kCLastScore + 1;   // max(1): slots 59..63
+          constexpr int kW1 = kM1 + 5;           // tile 1, keys 0..7: slots 64..67
+          static_assert(kE0 + 4 == kCPrefix && kCPrefix == kCFirstOut && kE1 + 6 * 3 < kCOutU1 &&
+                            kW1 + 4 == kCSlots,
+                        "combined chain payload layout");
+          auto pay_c = [&](auto slot) {
+            constexpr int k = decltype(slot)::value;
+            if constexpr (k < kE0) {
+              if constexpr (k == 0) mask(sc0, vis0);
+              max_part(sc0, slot);
+            } else if constexpr (k < kE0 + 4) {
+              weight2(sc0, ic<2 * (k - kE0)>{});
+              if constexpr (k == kE0 + 3)
+                pop[0] = __builtin_bit_cast(bf16x8, (u32x4){pk[0], pk[1], pk[2], pk[3]});
+            } else if constexpr (k >= kE1 && k <= kE1 + 6 * 3 && (k - kE1) % 6 == 0) {
+              weight2(sc0, ic<8 + 2 * ((k - kE1) / 6)>{});
+              if constexpr (k == kE1 + 6 * 3) {
+                pop[1] = __builtin_bit_cast(bf16x8, (u32x4){pk[4], pk[5], pk[6], pk[7]});
+                fold_ls();
+              }
+            } else if constexpr (k >= kM1 && k < kM1 + 5) {
+              // the last score MFMA went out one slot before: let its result land
+              if constexpr (k == kM1) {
+                asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+                MLA_SB();  // (reads of sc1 stay below the wait states)
+                mask(sc1, vis1);
+              }
+              max_part(sc1, ic<k - kM1>{});
+            } else if constexpr (k >= kW1) {
+              weight2(sc1, ic<2 * (k - kW1)>{});
+            }
+          };
+          auto hook_c = [&](auto slot) {
+            constexpr int k = decltype(slot)::value;
+            if constexpr (k == kE0 - 1) {
+              need = m_tile > m_run + kTau;
+              if (__any(need)) rescale();
+              neg_m = m_run == -INFINITY ? 0.f : -m_run;
+  #pragma unroll
+              for (int j = 0; j < 4; ++j) ls[j] = 0.f;
+            } else if constexpr (k == kW1 - 1) {
+              need = m_tile > m_run + kTau;
+            } else if constexpr (!FP8 && k >= kLd && k <= kLd + 3 * 8 && (k - kLd) % 3 == 0) {
+              load(ic<9 + (k - kLd) / 3>{});
+            }
+          };
+          combined_chain(sc1, oacc, pop, qreg, ka, va, hook_c, pay_c);
+          prefetch_q();
+          redo_tile1();
+          pv_tile<1>(oacc, pop, va, no_hook, pay_pv1);
+        }
       }
     };
 
@@ -1349,39 +1693,45 @@ extern "C" mla_status mla_decode_time_next_launch(hipEvent_t start, hipEvent_t s
   return mla::ok();
 }
 
-extern "C" mla_status mla_decode(const void* q, int32_t bs, int32_t q_len, int32_t num_heads,
-                                 const void* kv_cache, int32_t kv_dtype, int64_t num_pages,
-                                 const int32_t* block_table, int32_t bt_row_stride,
-                                 const int32_t* seq_lens, const int32_t* tile_plan,
-                                 int32_t num_parts, const int32_t* split_indptr,
-                                 float softmax_scale, int32_t causal, const float* kv_descale,
-                                 void* partial_o, float* partial_lse, int32_t partial_slots,
-                                 void* out, float* lse, hipStream_t stream) {
-  using namespace mla;
+namespace mla {
+namespace {
+
+// mla_decode and mla_decode_q8: checks, then the launch.  q8: q holds e4m3
+// codes scaled by *q_descale, over an e4m3 cache.
+mla_status decode_impl(const char* name, const void* q, const float* q_descale, bool q8,
+                       int32_t bs, int32_t q_len, int32_t num_heads, const void* kv_cache,
+                       int32_t kv_dtype, int64_t num_pages, const int32_t* block_table,
+                       int32_t bt_row_stride, const int32_t* seq_lens, const int32_t* tile_plan,
+                       int32_t num_parts, const int32_t* split_indptr, float softmax_scale,
+                       int32_t causal, const float* kv_descale, void* partial_o,
+                       float* partial_lse, int32_t partial_slots, void* out, float* lse,
+                       hipStream_t stream) {
+  const std::string n(name);
   const hipEvent_t ev_start = t_start_event, ev_stop = t_stop_event;
   t_start_event = t_stop_event = nullptr;
   if (!q || !kv_cache || !block_table || !seq_lens || !tile_plan || !split_indptr || !partial_o ||
-      !partial_lse || !out)
-    return fail(MLA_ERR_INVALID_ARGUMENT, "mla_decode: null pointer");
+      !partial_lse || !out || (q8 && !q_descale))
+    return fail(MLA_ERR_INVALID_ARGUMENT, n + ": null pointer");
   if (bs <= 0 || q_len <= 0 || num_heads <= 0 || num_pages <= 0 || bt_row_stride <= 0 ||
       num_parts <= 0)
-    return fail(MLA_ERR_INVALID_ARGUMENT, "mla_decode: sizes must be positive");
+    return fail(MLA_ERR_INVALID_ARGUMENT, n + ": sizes must be positive");
   if (!finite_nonneg(softmax_scale))
-    return fail(MLA_ERR_INVALID_ARGUMENT, "mla_decode: softmax_scale must be finite and >= 0");
+    return fail(MLA_ERR_INVALID_ARGUMENT, n + ": softmax_scale must be finite and >= 0");
   if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3)
-    return fail(MLA_ERR_UNSUPPORTED, "mla_decode: unknown kv_dtype");
+    return fail(MLA_ERR_UNSUPPORTED, n + ": unknown kv_dtype");
+  if (q8 && kv_dtype != MLA_KV_FP8_E4M3)
+    return fail(MLA_ERR_UNSUPPORTED, n + ": an e4m3 query needs an e4m3 cache");
   if (kv_dtype == MLA_KV_FP8_E4M3 && !kv_descale)
-    return fail(MLA_ERR_INVALID_ARGUMENT, "mla_decode: fp8 cache needs kv_descale");
+    return fail(MLA_ERR_INVALID_ARGUMENT, n + ": fp8 cache needs kv_descale");
   const int64_t rows = (int64_t)q_len * num_heads;
   if (rows < 1 || rows > MLA_MAX_ROWS_PER_REQ)
-    return fail(MLA_ERR_UNSUPPORTED, "mla_decode: q_len*num_heads must be in 1..512");
+    return fail(MLA_ERR_UNSUPPORTED, n + ": q_len*num_heads must be in 1..512");
   if (num_parts > MLA_MAX_DECODE_PARTS)
-    return fail(MLA_ERR_CAPACITY,
-                "mla_decode: num_parts above " + std::to_string(MLA_MAX_DECODE_PARTS));
+    return fail(MLA_ERR_CAPACITY, n + ": num_parts above " + std::to_string(MLA_MAX_DECODE_PARTS));
   if ((int64_t)bs * bt_row_stride >= (int64_t)1 << 29)
-    return fail(MLA_ERR_UNSUPPORTED, "mla_decode: the block table must hold fewer than 2^29 entries");
+    return fail(MLA_ERR_UNSUPPORTED, n + ": the block table must hold fewer than 2^29 entries");
   if ((int64_t)partial_slots < (int64_t)bs + num_parts)
-    return fail(MLA_ERR_CAPACITY, "mla_decode: partial_slots must be at least bs + num_parts");
+    return fail(MLA_ERR_CAPACITY, n + ": partial_slots must be at least bs + num_parts");
 
   DecodeParams p;
   p.num_pages = num_pages;
@@ -1394,23 +1744,58 @@ extern "C" mla_status mla_decode(const void* q, int32_t bs, int32_t q_len, int32
   p.causal = causal ? 1 : 0;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   dim3 grid(num_parts, (unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
-  auto launch = [&](auto kernel, const float* descale) {
+  auto launch = [&](auto kernel) {
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(q);
     const uint8_t* kvp = reinterpret_cast<const uint8_t*>(kv_cache);
+    const float* kd = kv_dtype == MLA_KV_FP8_E4M3 ? kv_descale : nullptr;
+    const float* qd = q8 ? q_descale : nullptr;
     uint16_t* op = reinterpret_cast<uint16_t*>(out);
     uint16_t* po = reinterpret_cast<uint16_t*>(partial_o);
     if (ev_start || ev_stop)
       hipExtLaunchKernelGGL(kernel, grid, dim3(kWaves * 64), 0, stream, ev_start, ev_stop, 0, qp,
-                            kvp, block_table, seq_lens, tile_plan, split_indptr, descale,
-                            po, partial_lse, op, lse, p);
+                            kvp, block_table, seq_lens, tile_plan, split_indptr, kd, qd, po,
+                            partial_lse, op, lse, p);
     else
       hipLaunchKernelGGL(kernel, grid, dim3(kWaves * 64), 0, stream, qp, kvp, block_table,
-                         seq_lens, tile_plan, split_indptr, descale, po, partial_lse, op,
-                         lse, p);
+                         seq_lens, tile_plan, split_indptr, kd, qd, po, partial_lse, op, lse, p);
   };
-  if (kv_dtype == MLA_KV_FP8_E4M3)
-    launch(mla_decode_kernel<true>, kv_descale);
+  if (q8)
+    launch(mla_decode_kernel<true, true>);
+  else if (kv_dtype == MLA_KV_FP8_E4M3)
+    launch(mla_decode_kernel<true, false>);
   else
-    launch(mla_decode_kernel<false>, nullptr);
-  return check_launch("mla_decode");
+    launch(mla_decode_kernel<false, false>);
+  return check_launch(name);
+}
+
+}  // namespace
+}  // namespace mla
+
+extern "C" mla_status mla_decode(const void* q, int32_t bs, int32_t q_len, int32_t num_heads,
+                                 const void* kv_cache, int32_t kv_dtype, int64_t num_pages,
+                                 const int32_t* block_table, int32_t bt_row_stride,
+                                 const int32_t* seq_lens, const int32_t* tile_plan,
+                                 int32_t num_parts, const int32_t* split_indptr,
+                                 float softmax_scale, int32_t causal, const float* kv_descale,
+                                 void* partial_o, float* partial_lse, int32_t partial_slots,
+                                 void* out, float* lse, hipStream_t stream) {
+  return mla::decode_impl("mla_decode", q, nullptr, false, bs, q_len, num_heads, kv_cache,
+                          kv_dtype, num_pages, block_table, bt_row_stride, seq_lens, tile_plan,
+                          num_parts, split_indptr, softmax_scale, causal, kv_descale, partial_o,
+                          partial_lse, partial_slots, out, lse, stream);
+}
+
+extern "C" mla_status mla_decode_q8(const void* q_fp8, const float* q_descale, int32_t bs,
+                                    int32_t q_len, int32_t num_heads, const void* kv_cache,
+                                    int64_t num_pages, const int32_t* block_table,
+                                    int32_t bt_row_stride, const int32_t* seq_lens,
+                                    const int32_t* tile_plan, int32_t num_parts,
+                                    const int32_t* split_indptr, float softmax_scale,
+                                    int32_t causal, const float* kv_descale, void* partial_o,
+                                    float* partial_lse, int32_t partial_slots, void* out,
+                                    float* lse, hipStream_t stream) {
+  return mla::decode_impl("mla_decode_q8", q_fp8, q_descale, true, bs, q_len, num_heads,
+                          kv_cache, MLA_KV_FP8_E4M3, num_pages, block_table, bt_row_stride,
+                          seq_lens, tile_plan, num_parts, split_indptr, softmax_scale, causal,
+                          kv_descale, partial_o, partial_lse, partial_slots, out, lse, stream);
 }

@@ -77,6 +77,31 @@ def test_decode_argument_errors(kw, status):
     assert _lib.lib().mla_last_error_message().startswith(b"mla_decode")
 
 
+def _decode_q8(**kw):
+    a = dict(q=FAKE, qd=FAKE, bs=2, q_len=1, heads=16, kv=FAKE, pages=8, bt=FAKE, bts=3,
+             sl=FAKE, tp=FAKE, parts=4, ip=FAKE, scale=0.07, causal=1, desc=FAKE, po=FAKE,
+             pl=FAKE, slots=6, out=FAKE, lse=None)
+    a.update(kw)
+    return _lib.lib().mla_decode_q8(a["q"], a["qd"], a["bs"], a["q_len"], a["heads"], a["kv"],
+                                    a["pages"], a["bt"], a["bts"], a["sl"], a["tp"], a["parts"],
+                                    a["ip"], a["scale"], a["causal"], a["desc"], a["po"],
+                                    a["pl"], a["slots"], a["out"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), _lib.MLA_ERR_INVALID_ARGUMENT),
+    (dict(qd=None), _lib.MLA_ERR_INVALID_ARGUMENT),           # no query descale
+    (dict(desc=None), _lib.MLA_ERR_INVALID_ARGUMENT),         # no cache descale
+    (dict(bs=0), _lib.MLA_ERR_INVALID_ARGUMENT),
+    (dict(scale=float("nan")), _lib.MLA_ERR_INVALID_ARGUMENT),
+    (dict(heads=513), _lib.MLA_ERR_UNSUPPORTED),
+    (dict(slots=5), _lib.MLA_ERR_CAPACITY),
+])
+def test_decode_q8_argument_errors(kw, status):
+    assert _decode_q8(**kw) == status
+    assert _lib.lib().mla_last_error_message().startswith(b"mla_decode_q8")
+
+
 def test_block_table_argument_errors():
     lib = _lib.lib()
     f = lib.mla_build_block_table

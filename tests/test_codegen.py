@@ -14,8 +14,8 @@ kernel has to cover by hand (counted in wait states: one per instruction,
 N + 1 for s_nop N):
   * a VALU write of a register an MFMA then reads needs 2 wait states;
   * an MFMA result read or overwritten by anything but the next MFMA of the
-    same accumulation needs 12 (what the compiler itself inserts after a
-    32x32x16 MFMA on gfx950).
+    same accumulation needs 12 after a 32x32x16 bf16 MFMA and 20 after a
+    32x32x64 e4m3 one (what the compiler itself inserts on gfx950).
 The walk follows the code in layout order, which for these straight-line
 chains is execution order.
 """
@@ -126,7 +126,8 @@ def _wait_states(ins):
 
 
 VALU_TO_MFMA = 2
-MFMA_TO_OTHER = 12
+MFMA_TO_OTHER = 12      # 32x32x16 bf16: 8 passes
+MFMA8_TO_OTHER = 20     # 32x32x64 f8f6f4 on e4m3 operands: 16 passes
 
 
 def _mfma_hazards(instrs):
@@ -147,8 +148,9 @@ def _mfma_hazards(instrs):
             j -= 1
         # (2) uses of the result shortly after
         dst = _regs(args[0])
+        need = MFMA8_TO_OTHER if "f8f6f4" in op else MFMA_TO_OTHER
         ws, j = 0, i + 1
-        while j < len(instrs) and ws < MFMA_TO_OTHER:
+        while j < len(instrs) and ws < need:
             nop, nargs = _split(instrs[j])
             if nop.startswith("v_mfma"):
                 same_acc = len(nargs) > 3 and _regs(nargs[3]) == dst and _regs(nargs[0]) == dst
@@ -179,10 +181,13 @@ def decode_asm():
     return _compile("decode.hip")
 
 
-def test_both_kernels_present(decode_asm):
-    """The page kernel in its two instances: bf16 cache and e4m3 cache."""
-    names = list(_kernels(decode_asm))
-    assert len(names) == 2, names
+def test_all_kernels_present(decode_asm):
+    """The page kernel in its three instances: bf16 cache, e4m3 cache, e4m3
+    cache with an e4m3 query (whose score MFMAs are the e4m3 ones)."""
+    bodies = _kernels(decode_asm)
+    assert len(bodies) == 3, list(bodies)
+    f8 = {n: sum("f8f6f4" in i for i in b) for n, b in bodies.items()}
+    assert sorted(f8.values())[:2] == [0, 0] and max(f8.values()) > 0, f8
 
 
 def test_no_instruction_touches_an_in_flight_lds_read(decode_asm):
@@ -235,3 +240,7 @@ def test_hazard_walk_flags_planted_cases():
     assert _mfma_hazards([mf, mf2]) == []
     assert _mfma_hazards([mf, "v_accvgpr_read_b32 v1, a3"]) != []
     assert _mfma_hazards([mf, "s_nop 7", "s_nop 3", "v_accvgpr_read_b32 v1, a3"]) == []
+    # the e4m3 MFMA needs longer before its result is read
+    f8 = "v_mfma_f32_32x32x64_f8f6f4 v[0:15], v[16:23], v[24:31], v[0:15]"
+    assert _mfma_hazards([f8, "s_nop 7", "s_nop 3", "v_mov_b32_e32 v40, v3"]) != []
+    assert _mfma_hazards([f8, "s_nop 7", "s_nop 7", "s_nop 3", "v_mov_b32_e32 v40, v3"]) == []
