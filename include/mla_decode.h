@@ -19,15 +19,24 @@
  *
  * Conventions shared by every entry point
  *   - Every pointer is device memory unless its comment says "host".
- *   - The caller owns every buffer.  The library allocates no device memory.
+ *   - The caller owns every buffer.  The library allocates no device memory
+ *     at run time; its only device memory of its own is file-scope arrays
+ *     (the static workspace of mla_decode_static; the debug build's error
+ *     word), held per device until the process ends.
  *     State kept between calls: per host thread, the last error text and the
  *     events of mla_decode_time_next_launch (used by the next decode only);
  *     per device, whether the planner kernels' LDS limit was raised (set
- *     once, on their first launch there).
+ *     once, on their first launch there) and the static workspace's address;
+ *     per process, whether MLA_TRACE is set (read once).
  *   - Calls are asynchronous on the given HIP stream (0 = the null stream),
  *     never synchronise and never read device memory on the host, so they can
  *     be captured in a HIP graph (the FlashMLA page prepares fixed-capacity
- *     buffers for graph replay in init_cuda_graph_state).
+ *     buffers for graph replay in init_cuda_graph_state).  The debug build
+ *     (libmla_decode_debug.so, compiled with -DMLA_DEBUG) is the exception:
+ *     the table builders and the decodes check their preconditions on the
+ *     device and synchronise the stream to read the result back.
+ *   - With the environment variable MLA_TRACE set (not "0"), every launch
+ *     writes one line to stderr ("[mla] entry point: sizes, grid, stream").
  *   - Argument errors are detected on the host before any launch and
  *     returned as a status; nothing is launched then.  No C++ exception
  *     crosses the ABI; no call aborts the process.
@@ -58,7 +67,7 @@ typedef enum mla_status {
   MLA_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, bad enum, non-finite scale */
   MLA_ERR_UNSUPPORTED = 2,      /* a shape or dtype this build has no kernel for */
   MLA_ERR_CAPACITY = 3,         /* a caller buffer is too small for the request */
-  MLA_ERR_PRECONDITION = 4,     /* reserved for debug builds */
+  MLA_ERR_PRECONDITION = 4,     /* debug build only: a device-side precondition check failed */
   MLA_ERR_DEVICE = 5            /* a HIP runtime call failed; see mla_last_error_message */
 } mla_status;
 
@@ -70,8 +79,9 @@ typedef enum mla_kv_dtype {
 /* Version of this ABI (MLA_ABI_VERSION of the build). */
 int32_t mla_abi_version(void);
 
-/* Static text for a status code. */
-const char* mla_status_string(mla_status status);
+/* Static text for a status code; any int32 value is accepted ("unknown
+ * status" for values that are not an mla_status). */
+const char* mla_status_string(int32_t status);
 
 /* Text describing the last non-OK status returned on this host thread
  * ("" if none).  Valid until the next library call on the thread. */
@@ -86,7 +96,10 @@ const char* mla_last_error_message(void);
  *     block_table[b * bt_row_stride + p] = floor(req_to_token[rpi[b] * r2t_row_stride + 64*p] / 64)
  * i.e. the page holding token 64p.  Every other cell of the row, up to
  * bt_row_stride, is written with pad_value (the page pre-fills with -1).
- * Slots are assumed page-aligned (slot of token j = 64*page + j % 64).
+ * Slots are assumed page-aligned (slot of token j = 64*page + j % 64); the
+ * debug build checks every token of every request against the table it
+ * built and returns PRECONDITION naming the first that differs (a table
+ * narrower than a request counts as well).
  *
  *   req_to_token      int32 [r2t_rows, r2t_row_stride]
  *   req_pool_indices  int32 [bs], each in [0, r2t_rows)
@@ -259,6 +272,8 @@ int32_t mla_device_num_cus(void);
  * Block-table entries outside [0, num_pages), or a page index at or past
  * bt_row_stride, are a caller error: such a page is never read, and its keys
  * are masked (they contribute nothing), so the kernel never leaves the pool.
+ * The debug build checks the entries first and returns PRECONDITION naming
+ * the first bad (request, page), launching nothing.
  *
  * Errors: INVALID_ARGUMENT for null pointers, non-positive sizes, a
  * negative or non-finite scale, or fp8 with a NULL kv_descale; UNSUPPORTED for

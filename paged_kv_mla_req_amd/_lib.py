@@ -11,6 +11,8 @@ import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmla_decode.so")
+# the debug build (-DMLA_DEBUG: device-side precondition checks, see build.py)
+DEBUG_LIB_PATH = os.path.join(_PKG, "libmla_decode_debug.so")
 
 MLA_OK = 0
 MLA_ERR_INVALID_ARGUMENT = 1
@@ -58,6 +60,7 @@ SIGNATURES = {
 }
 
 _lib = None
+_debug_lib = None
 
 
 class MLAError(RuntimeError):
@@ -66,20 +69,33 @@ class MLAError(RuntimeError):
         self.status = status
 
 
+def load(path: str) -> ctypes.CDLL:
+    """Load one build of the library and declare every entry point's types."""
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m paged_kv_mla_req_amd.build`")
+    handle = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.restype = res
+        fn.argtypes = args
+    return handle
+
+
 def lib() -> ctypes.CDLL:
     """The loaded library; raises if it has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(
-                f"{LIB_PATH} is missing: build it with `python -m paged_kv_mla_req_amd.build`")
-        handle = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in SIGNATURES.items():
-            fn = getattr(handle, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = handle
+        _lib = load(LIB_PATH)
     return _lib
+
+
+def debug_lib() -> ctypes.CDLL:
+    """The debug build (a separate copy of the library, for tests of its
+    precondition checks); raises if it has not been built."""
+    global _debug_lib
+    if _debug_lib is None:
+        _debug_lib = load(DEBUG_LIB_PATH)
+    return _debug_lib
 
 
 def check(status: int) -> None:

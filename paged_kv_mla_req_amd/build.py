@@ -1,8 +1,15 @@
-"""Build the gfx950 shared library ``libmla_decode.so`` in-tree with hipcc.
+"""Build the gfx950 shared library ``libmla_decode.so`` in-tree with hipcc,
+and its debug build ``libmla_decode_debug.so``.
 
 Usage: ``python -m paged_kv_mla_req_amd.build`` (or ``build()`` from Python).
 Every source is compiled for gfx950 only; objects go to ``_build/`` next to
-this file and the library is linked into the package directory.
+this file and the libraries are linked into the package directory.
+
+The debug build is the same sources compiled with ``-DMLA_DEBUG`` plus
+``debug_checks.hip``: the table builders and the decode check their
+preconditions on the device (page-aligned slots, block-table entries inside
+the table and the pool) and return MLA_ERR_PRECONDITION, synchronising the
+stream to do so.  The kernels themselves are the release kernels.
 """
 
 from __future__ import annotations
@@ -19,8 +26,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmla_decode.so")
+DEBUG_LIB = os.path.join(PKG, "libmla_decode_debug.so")
 SOURCES = ["abi.hip", "block_table.hip", "plan.hip", "decode.hip", "merge.hip", "append.hip",
            "noalloc.hip"]
+DEBUG_SOURCES = SOURCES + ["debug_checks.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms stay disabled: the compiler would otherwise emit
@@ -52,29 +61,37 @@ def _run(cmd):
     return res
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    """Compile every source and link ``libmla_decode.so``; returns its path."""
+def _build_one(sources, lib, extra, tag, verbose, jobs) -> str:
     hipcc = _hipcc()
     os.makedirs(BUILD, exist_ok=True)
 
     def compile_one(src):
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        cmd = [hipcc, *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
-               "-o", obj]
+        obj = os.path.join(BUILD, src.replace(".hip", tag + ".o"))
+        cmd = [hipcc, *COMMON_FLAGS, *extra, *SOURCE_FLAGS.get(src, []), "-c",
+               os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         _run(cmd)
         return obj
 
-    with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(SOURCES)))) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
+    with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(sources)))) as ex:
+        objs = list(ex.map(compile_one, sources))
+    tmp = lib + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     _run(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False, jobs: int = 8, debug: bool = True) -> str:
+    """Compile every source and link ``libmla_decode.so`` (and, with `debug`,
+    ``libmla_decode_debug.so``); returns the release library's path."""
+    path = _build_one(SOURCES, LIB, [], "", verbose, jobs)
+    if debug:
+        _build_one(DEBUG_SOURCES, DEBUG_LIB, ["-DMLA_DEBUG"], ".debug", verbose, jobs)
+    return path
 
 
 if __name__ == "__main__":

@@ -1,5 +1,9 @@
-// Status codes, error text and host helpers of the C ABI.
+// Status codes, error text, the launch log and host helpers of the C ABI.
 #include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <string>
 
 #include "common.h"
@@ -20,6 +24,24 @@ mla_status ok() {
 
 bool finite_nonneg(float x) { return std::isfinite(x) && x >= 0.f; }
 
+bool trace_on() {
+  static const bool on = [] {
+    const char* e = std::getenv("MLA_TRACE");
+    return e && *e && std::strcmp(e, "0") != 0;
+  }();
+  return on;
+}
+
+void trace(const char* fmt, ...) {
+  if (!trace_on()) return;
+  char line[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(line, sizeof(line), fmt, ap);
+  va_end(ap);
+  std::fprintf(stderr, "[mla] %s\n", line);
+}
+
 mla_status check_launch(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess)
@@ -33,7 +55,7 @@ extern "C" {
 
 int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
 
-const char* mla_status_string(mla_status status) {
+const char* mla_status_string(int32_t status) {
   switch (status) {
     case MLA_OK: return "ok";
     case MLA_ERR_INVALID_ARGUMENT: return "invalid argument";

@@ -104,6 +104,8 @@ extern "C" mla_status mla_set_kv_buffer(const void* k, int64_t k_row_stride,
   const int64_t num_slots = num_pages * kPage;
   const uint16_t* kk = static_cast<const uint16_t*>(k);
   uint8_t* dst = static_cast<uint8_t*>(kv_cache);
+  trace("mla_set_kv_buffer: tokens %d kv_dtype %d pages %lld grid %u stream %p", num_tokens,
+        kv_dtype, (long long)num_pages, blocks, (void*)stream);
   if (fp8)
     set_kv_kernel<true><<<blocks, kAppendThreads, 0, stream>>>(kk, k_row_stride, out_cache_loc,
                                                                num_tokens, dst, num_slots, kv_scale);
@@ -131,6 +133,8 @@ extern "C" mla_status mla_quantize_q_fp8(const void* q, int64_t q_row_stride, in
   if (num_rows == 0) return ok();
   const int64_t threads = num_rows * kAppendChunks;
   const unsigned blocks = (unsigned)((threads + kAppendThreads - 1) / kAppendThreads);
+  trace("mla_quantize_q_fp8: rows %lld grid %u stream %p", (long long)num_rows, blocks,
+        (void*)stream);
   set_kv_kernel<true><<<blocks, kAppendThreads, 0, stream>>>(
       static_cast<const uint16_t*>(q), q_row_stride, nullptr, (int32_t)num_rows,
       static_cast<uint8_t*>(q_fp8), num_rows, q_scale);

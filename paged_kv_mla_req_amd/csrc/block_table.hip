@@ -60,8 +60,18 @@ extern "C" mla_status mla_build_block_table(const int32_t* req_to_token, int32_t
       seq_lens, bs, page_size, block_table, bt_row_stride, max_seq_len_hint);
   if (st != MLA_OK) return st;
   dim3 grid((bt_row_stride + 255) / 256, bs);
+  trace("mla_build_block_table: bs %d width %d grid %ux%u stream %p", bs, bt_row_stride, grid.x,
+        grid.y, (void*)stream);
   hipLaunchKernelGGL(build_block_table_kernel, grid, dim3(256), 0, stream, req_to_token,
                      r2t_rows, r2t_row_stride, req_pool_indices, seq_lens, block_table,
                      bt_row_stride, pad_value);
+#ifdef MLA_DEBUG
+  const mla_status launched = check_launch("mla_build_block_table");
+  if (launched != MLA_OK) return launched;
+  return debug_check_page_aligned("mla_build_block_table", req_to_token, r2t_rows, r2t_row_stride,
+                                  req_pool_indices, seq_lens, bs, block_table, bt_row_stride,
+                                  stream);
+#else
   return check_launch("mla_build_block_table");
+#endif
 }

@@ -1744,6 +1744,17 @@ mla_status decode_impl(const char* name, const void* q, const float* q_descale, 
   p.causal = causal ? 1 : 0;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   dim3 grid(num_parts, (unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+#ifdef MLA_DEBUG
+  {
+    const mla_status checked = debug_check_table_entries(name, block_table, bt_row_stride,
+                                                         seq_lens, bs, num_pages, stream);
+    if (checked != MLA_OK) return checked;
+  }
+#endif
+  trace("%s: bs %d q_len %d heads %d kv_dtype %d%s pages %lld width %d parts %d slots %d "
+        "grid %ux%u stream %p",
+        name, bs, q_len, num_heads, kv_dtype, q8 ? " (e4m3 query)" : "", (long long)num_pages,
+        bt_row_stride, num_parts, partial_slots, grid.x, grid.y, (void*)stream);
   auto launch = [&](auto kernel) {
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(q);
     const uint8_t* kvp = reinterpret_cast<const uint8_t*>(kv_cache);

@@ -158,6 +158,8 @@ extern "C" mla_status mla_merge_states(const void* partial_o, const float* parti
   const int64_t waves = (int64_t)bs * rows_per_req;
   const int64_t blocks = (waves + kMergeWaves - 1) / kMergeWaves;
   if (blocks > 0x7fffffff) return fail(MLA_ERR_UNSUPPORTED, "mla_merge_states: too many rows");
+  trace("mla_merge_states: bs %d rows %d slots %d grid %lld stream %p", bs, rows_per_req,
+        partial_slots, (long long)blocks, (void*)stream);
   hipLaunchKernelGGL(merge_states_kernel, dim3((unsigned)blocks), dim3(64 * kMergeWaves), 0,
                      stream, reinterpret_cast<const uint16_t*>(partial_o), partial_lse,
                      partial_slots, split_indptr, bs, rows_per_req,

@@ -486,6 +486,8 @@ extern "C" mla_status mla_plan_splits(const int32_t* seq_lens, int32_t bs, int32
   static std::atomic<bool> lds_raised[kMaxDevices];
   const mla_status la = allow_plan_lds(plan_splits_kernel, lds_raised, "mla_plan_splits");
   if (la != MLA_OK) return la;
+  trace("mla_plan_splits: bs %d rows %d parts %d lds %zu stream %p", bs, rows_per_req, num_parts,
+        lds, (void*)stream);
   hipLaunchKernelGGL(plan_splits_kernel, dim3(1), dim3(kPlanThreads), lds, stream, seq_lens, bs,
                      overhead, num_parts, tile_plan, split_indptr);
   return check_launch("mla_plan_splits");
@@ -513,11 +515,20 @@ extern "C" mla_status mla_build_table_and_plan(
   static std::atomic<bool> lds_raised[kMaxDevices];
   st = allow_plan_lds(table_and_plan_kernel, lds_raised, who);
   if (st != MLA_OK) return st;
+  trace("%s: bs %d width %d rows %d parts %d grid %lld lds %zu stream %p", who, bs,
+        bt_row_stride, rows_per_req, num_parts, (long long)blocks, lds, (void*)stream);
   hipLaunchKernelGGL(table_and_plan_kernel, dim3((unsigned)blocks), dim3(kPlanThreads), lds,
                      stream, req_to_token, r2t_rows, r2t_row_stride, req_pool_indices, seq_lens,
                      block_table, bt_row_stride, pad_value, per_row, bs,
                      plan_overhead_q(rows_per_req), num_parts, tile_plan, split_indptr);
+#ifdef MLA_DEBUG
+  st = check_launch(who);
+  if (st != MLA_OK) return st;
+  return debug_check_page_aligned(who, req_to_token, r2t_rows, r2t_row_stride, req_pool_indices,
+                                  seq_lens, bs, block_table, bt_row_stride, stream);
+#else
   return check_launch(who);
+#endif
 }
 
 // ---------------------------------------------------------------------------
@@ -616,6 +627,8 @@ extern "C" mla_status mla_plan_fixed_splits(const int32_t* seq_lens, int32_t bs,
     return fail(MLA_ERR_CAPACITY, w + ": " + std::to_string(bs) + " requests of up to " +
                                       std::to_string(max_seq_len_hint) +
                                       " tokens may need more than max_parts pieces");
+  trace("%s: bs %d tile_pages %d max_parts %d stream %p", w.c_str(), bs, tile_pages, max_parts,
+        (void*)stream);
   hipLaunchKernelGGL(plan_fixed_kernel, dim3(1), dim3(kPlanThreads), 0, stream, seq_lens, bs,
                      tile_pages, max_parts, tile_plan, split_indptr);
   return check_launch(w.c_str());
