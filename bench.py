@@ -172,31 +172,38 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, calib_mib: int, root: 
     import hashlib
 
     def read(path, counter):
-        dec, cal = [], []
+        """(scaled bytes per decode dispatch, scale, raw bytes, scaled bytes
+        per merge dispatch); counters summed over a dispatch's instances."""
+        per = {}
         with open(path) as f:
             for r in csv.DictReader(f):
                 if r["Counter_Name"] != counter:
                     continue
-                v = float(r["Counter_Value"]) * 1024.0
-                if "mla_decode" in r["Kernel_Name"] and "kernel" in r["Kernel_Name"]:
-                    dec.append(v)
-                elif "bitwise_not" in r["Kernel_Name"].lower():
-                    cal.append(v)
+                key = (r["Dispatch_Id"], r["Kernel_Name"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"]) * 1024.0
+        dec = [v for (_, k), v in per.items() if "mla_decode_kernel" in k]
+        mrg = [v for (_, k), v in per.items() if "merge_states_kernel" in k]
+        cal = [v for (_, k), v in per.items() if "bitwise_not" in k.lower()]
         if not dec or not cal:
             raise SystemExit(f"{path}: no decode or calibration dispatches for {counter}")
         factor = calib_mib * 2.0**20 / max(cal)
-        return float(np.mean(dec)) * factor, factor, float(np.mean(dec))
+        merge = float(np.mean(mrg)) * factor if mrg else None
+        return float(np.mean(dec)) * factor, factor, float(np.mean(dec)), merge
 
-    fetch, f_fac, f_raw = read(fetch_csv, "FETCH_SIZE")
-    write, w_fac, w_raw = read(write_csv, "WRITE_SIZE")
+    fetch, f_fac, f_raw, m_fetch = read(fetch_csv, "FETCH_SIZE")
+    write, w_fac, w_raw, m_write = read(write_csv, "WRITE_SIZE")
     src = _kernel_src(root, workload)
     with open(src, "rb") as f:
         sha = hashlib.sha256(f.read()).hexdigest()
-    return {"hbm_bytes_per_launch": round(fetch + write), "fetch_bytes": round(fetch),
-            "write_bytes": round(write), "fetch_raw_bytes": round(f_raw),
-            "write_raw_bytes": round(w_raw), "fetch_scale": round(f_fac, 4),
-            "write_scale": round(w_fac, 4), "calibration_mib": calib_mib,
-            "kernel_source_sha256": sha}
+    rec = {"hbm_bytes_per_launch": round(fetch + write), "fetch_bytes": round(fetch),
+           "write_bytes": round(write), "fetch_raw_bytes": round(f_raw),
+           "write_raw_bytes": round(w_raw), "fetch_scale": round(f_fac, 4),
+           "write_scale": round(w_fac, 4), "calibration_mib": calib_mib,
+           "kernel_source_sha256": sha}
+    if m_fetch is not None and m_write is not None:
+        rec["merge"] = {"hbm_bytes_per_launch": round(m_fetch + m_write),
+                        "fetch_bytes": round(m_fetch), "write_bytes": round(m_write)}
+    return rec
 
 
 def cpu_baseline(w, runs: int) -> dict:

@@ -10,7 +10,8 @@
 // A piece's o is stored in bf16 (normalised by its own row sum) and its lse in
 // fp32.  One wave per (request, row): each lane owns 8 of the 512 value
 // columns, one 16-byte load per piece, so a piece's row is one coalesced
-// 1 KiB read, with the rows of sixteen pieces in flight at a time; for up to
+// 1 KiB read, with the rows of eight pieces in flight at a time (63 VGPRs: eight
+// waves per SIMD, so the whole DeepSeek-V3-shaped batch is resident at once); for up to
 // 64 pieces the lanes take one piece's lse each (wave max and sum) while the
 // first rows are already loading, so a row costs one memory round trip.
 // Pure HBM streaming; no MFMA.
@@ -19,7 +20,8 @@
 namespace mla {
 
 constexpr int kMergeWaves = 4;
-constexpr int kMergeBatch = 16;  // pieces whose rows are loaded together
+constexpr int kXcdsMerge = 8;  // accelerator dies, each with its own L2
+constexpr int kMergeBatch = 8;   // pieces whose rows are loaded together
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -52,7 +54,14 @@ merge_states_kernel(const uint16_t* __restrict__ partial_o, const float* __restr
                     int partial_slots, const int32_t* __restrict__ split_indptr, int bs,
                     int rows, uint16_t* __restrict__ out, float* __restrict__ lse_out) {
   const int lane = threadIdx.x & 63;
-  const int64_t gw = (int64_t)blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
+  // Work-groups go to the dies round robin (work-group i to die i % 8).  The
+  // decode leaves each die a contiguous run of parts, i.e. of requests, so
+  // the merge gives each die a contiguous run of rows as well: most of a
+  // request's partial rows are then read on the die that wrote them.
+  const int64_t nblk = gridDim.x, per = nblk / kXcdsMerge, extra = nblk % kXcdsMerge;
+  const int64_t x = blockIdx.x % kXcdsMerge, j = blockIdx.x / kXcdsMerge;
+  const int64_t blk = x * per + (x < extra ? x : extra) + j;
+  const int64_t gw = blk * kMergeWaves + (threadIdx.x >> 6);
   if (gw >= (int64_t)bs * rows) return;
   const int b = (int)(gw / rows);
   const int r = (int)(gw - (int64_t)b * rows);
