@@ -33,10 +33,14 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on_gpu(t: torch.Tensor) -> bool:
+    return t.is_cuda
+
+
 def _need(t: torch.Tensor, name: str, dtypes, ndim: Optional[int] = None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a tensor")
-    if not t.is_cuda:
+    if not _on_gpu(t):
         raise ValueError(f"{name} must be on a GPU")
     if t.dtype not in dtypes:
         raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
@@ -411,7 +415,7 @@ def set_kv_buffer(kv_cache: torch.Tensor, out_cache_loc: torch.Tensor, k: torch.
     if kv_cache.shape[1:] != (PAGE_SIZE, LATENT_DIM):
         raise ValueError(f"kv_cache must be [pages, 64, 576], got {tuple(kv_cache.shape)}")
     _need(out_cache_loc, "out_cache_loc", (torch.int64,), 1)
-    if not isinstance(k, torch.Tensor) or not k.is_cuda or k.dtype != torch.bfloat16:
+    if not isinstance(k, torch.Tensor) or not _on_gpu(k) or k.dtype != torch.bfloat16:
         raise TypeError("k must be a bf16 GPU tensor")
     if k.dim() != 2 or k.shape[1] != LATENT_DIM or k.stride(1) != 1:
         raise ValueError("k must be [n, 576] with unit column stride")
