@@ -126,17 +126,28 @@ def measured_copy_gbs(torch, mib: int = 2048, reps: int = 10) -> float:
 
 
 def _kernel_of(kv_dtype: str, q8: bool = False):
-    """(source file under csrc/, kernel name) of the decode kernel that runs
+    """(source files under csrc/, kernel name) of the decode kernel that runs
     for a cache dtype (and an e4m3 query)."""
-    if kv_dtype == "bf16":
-        return "decode.hip", "mla_decode_kernel<false, false>"
-    return "decode.hip", "mla_decode_kernel<true, true>" if q8 else "mla_decode_kernel<true, false>"
+    if q8:
+        return ("decode_q8.hip", "decode_device.h"), "mla_decode_q8_kernel"
+    return ("decode.hip", "decode_device.h"), ("mla_decode_kernel<false>" if kv_dtype == "bf16"
+                                               else "mla_decode_kernel<true>")
 
 
-def _kernel_src(root: str, workload: str) -> str:
+def _kernel_src(root: str, workload: str, q8: bool = False) -> list:
     from workloads import CONFIGS
-    return os.path.join(root, "paged_kv_mla_req_amd", "csrc",
-                        _kernel_of(CONFIGS[workload]["kv_dtype"])[0])
+    return [os.path.join(root, "paged_kv_mla_req_amd", "csrc", f)
+            for f in _kernel_of(CONFIGS[workload]["kv_dtype"], q8)[0]]
+
+
+def _sources_sha(paths) -> str:
+    """sha256 over the kernel's source files, in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def _traffic_path(root: str, workload: str, q8: bool = False) -> str:
@@ -145,17 +156,15 @@ def _traffic_path(root: str, workload: str, q8: bool = False) -> str:
     return os.path.join(root, "profiles", f"mla_decode_{tag}_{workload}_traffic.json")
 
 
-def _traffic(root: str, kernel_src: str, workload: str, q8: bool = False):
+def _traffic(root: str, kernel_src, workload: str, q8: bool = False):
     """HBM bytes per decode launch from the committed counter summary, or None
     when that summary is missing or was taken on another version of the
-    kernel source (sha256 recorded in the file)."""
-    import hashlib
+    kernel's sources (sha256 recorded in the file)."""
     path = _traffic_path(root, workload, q8)
     try:
         with open(path) as f:
             rec = json.load(f)
-        with open(kernel_src, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        sha = _sources_sha(kernel_src)
     except (OSError, ValueError):
         return None
     if rec.get("kernel_source_sha256") != sha:
@@ -169,7 +178,8 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, calib_mib: int, root: 
     dispatch), each scaled by calib_mib MiB over what the same counter read
     for the calibration kernel (bitwise not over calib_mib MiB)."""
     import csv
-    import hashlib
+
+    name = _kernel_of("fp8_e4m3" if q8 else "bf16", q8)[1].split("<")[0]
 
     def read(path, counter):
         """(scaled bytes per decode dispatch, scale, raw bytes, scaled bytes
@@ -181,7 +191,7 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, calib_mib: int, root: 
                     continue
                 key = (r["Dispatch_Id"], r["Kernel_Name"])
                 per[key] = per.get(key, 0.0) + float(r["Counter_Value"]) * 1024.0
-        dec = [v for (_, k), v in per.items() if "mla_decode_kernel" in k]
+        dec = [v for (_, k), v in per.items() if name + "(" in k or name + "<" in k]
         mrg = [v for (_, k), v in per.items() if "merge_states_kernel" in k]
         cal = [v for (_, k), v in per.items() if "bitwise_not" in k.lower()]
         if not dec or not cal:
@@ -192,9 +202,7 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, calib_mib: int, root: 
 
     fetch, f_fac, f_raw, m_fetch = read(fetch_csv, "FETCH_SIZE")
     write, w_fac, w_raw, m_write = read(write_csv, "WRITE_SIZE")
-    src = _kernel_src(root, workload)
-    with open(src, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
+    sha = _sources_sha(_kernel_src(root, workload, q8))
     rec = {"hbm_bytes_per_launch": round(fetch + write), "fetch_bytes": round(fetch),
            "write_bytes": round(write), "fetch_raw_bytes": round(f_raw),
            "write_raw_bytes": round(w_raw), "fetch_scale": round(f_fac, 4),
@@ -398,13 +406,13 @@ class Path:
 
 
 def mfma_floor_ms(w, q8: bool) -> float:
-    """Matrix-core time floor of one decode launch at the dense peaks: the
-    scores at the e4m3 peak for an fp8 query, else everything at bf16."""
+    """Matrix-core time floor of one decode launch at the dense peaks of the
+    operand type: everything at the e4m3 peak for an fp8 query (the
+    algorithmic flops; the kernel's split of each weight into two e4m3
+    numbers doubles its output MFMAs, which this floor does not count), else
+    everything at bf16."""
     flops = _algorithmic_flops(w)
-    if not q8:
-        return flops / (MFMA_PEAK_TFLOPS * 1e12) * 1e3
-    score = flops * 576 / (576 + 512)
-    return (score / (MFMA_F8_PEAK_TFLOPS * 1e12) + (flops - score) / (MFMA_PEAK_TFLOPS * 1e12)) * 1e3
+    return flops / ((MFMA_F8_PEAK_TFLOPS if q8 else MFMA_PEAK_TFLOPS) * 1e12) * 1e3
 
 
 def measure_workload(mla, torch, name: str, q8: bool, steps: int, warmup: int,
@@ -447,7 +455,7 @@ def measure_workload(mla, torch, name: str, q8: bool, steps: int, warmup: int,
                  "achieved_tflops": round(flops / (dec_ms * 1e-3) / 1e12, 2),
                  "floor_us": round(mfma_floor_ms(w, q8) * 1e3, 2),
                  "frac": round(mfma_floor_ms(w, q8) / dec_ms, 4),
-                 "peaks": "e4m3 5000 TFLOP/s for the scores, bf16 2500 for the output"
+                 "peaks": "e4m3 5000 TFLOP/s"
                           if q8 else "bf16 2500 TFLOP/s"},
     }
     del P
@@ -603,7 +611,7 @@ def main() -> int:
                  "achieved_tflops": round(tflops, 2),
                  "floor_us": round(mfma_floor_ms(w, a.q8) * 1e3, 2),
                  "frac": round(mfma_floor_ms(w, a.q8) / dec_ms, 4),
-                 "peaks": "e4m3 5000 TFLOP/s for the scores, bf16 2500 for the output"
+                 "peaks": "e4m3 5000 TFLOP/s"
                           if a.q8 else "bf16 2500 TFLOP/s (an e4m3 cache is converted to "
                                        "bf16 in LDS)"},
         "append": append,
@@ -615,7 +623,7 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": _traffic(root, _kernel_src(root, a.workload), a.workload, a.q8),
+            "traffic": _traffic(root, _kernel_src(root, a.workload, a.q8), a.workload, a.q8),
             "kernel": _kernel_of(w.kv_dtype, a.q8)[1],
             "bytes_per_launch": b["total"],
         },

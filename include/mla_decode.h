@@ -298,8 +298,10 @@ mla_status mla_decode(const void* q, int32_t bs, int32_t q_len, int32_t num_head
  * q_r = e4m3fn(q_fp8 code) * (*q_descale) and the cache value
  * e4m3fn(byte) * (*kv_descale).  The scores are sums of exact products of
  * e4m3 codes (matrix cores, fp32 accumulation) times
- * softmax_scale * q_descale * kv_descale; the weights and V enter the output
- * contraction in bf16 (V exactly), accumulated in fp32, as in mla_decode.
+ * softmax_scale * q_descale * kv_descale; the output contraction also runs
+ * on e4m3 operands, V as stored and each weight as the sum of two e4m3
+ * numbers (about 2^-8 relative, against bf16's 2^-9 in mla_decode), scaled
+ * by a power of two per page, accumulated in fp32.
  *
  *   q_fp8      uint8 e4m3fn codes [bs, q_len, num_heads, 576], contiguous,
  *              16-byte aligned

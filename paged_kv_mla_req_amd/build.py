@@ -27,8 +27,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmla_decode.so")
 DEBUG_LIB = os.path.join(PKG, "libmla_decode_debug.so")
-SOURCES = ["abi.hip", "block_table.hip", "plan.hip", "decode.hip", "merge.hip", "append.hip",
-           "noalloc.hip"]
+SOURCES = ["abi.hip", "block_table.hip", "plan.hip", "decode.hip", "decode_q8.hip", "merge.hip",
+           "append.hip", "noalloc.hip"]
 DEBUG_SOURCES = SOURCES + ["debug_checks.hip"]
 ARCH = "gfx950"
 
@@ -44,7 +44,7 @@ COMMON_FLAGS = [
 # scores is a plain v_max/v_max3 (no operand canonicalisation).  No NaN
 # reaches it from the cache's unused slots: page tails are zero-filled, and
 # masked scores are -inf, scaled by a factor kept above 0.
-SOURCE_FLAGS = {"decode.hip": ["-fno-honor-nans"]}
+SOURCE_FLAGS = {"decode.hip": ["-fno-honor-nans"], "decode_q8.hip": ["-fno-honor-nans"]}
 
 
 def _hipcc() -> str:

@@ -41,15 +41,15 @@ def test_fp8_bytes_are_one_per_element():
 
 
 def test_q8_query_bytes_and_mfma_floor():
-    """An e4m3 query is one byte per value; its matrix floor prices the scores
-    (576 of the 1088 flop per pair) at the 5 PFLOP/s e4m3 peak and the output
-    at the 2.5 PFLOP/s bf16 peak."""
+    """An e4m3 query is one byte per value; its matrix floor prices the
+    algorithmic flops (1088 per pair: scores and output, both on e4m3
+    operands) at the 5 PFLOP/s e4m3 peak."""
     w = make_custom("f", bs=2, heads=16, q_len=1, seq_lens=[100, 64], seed=1,
                     kv_dtype="fp8_e4m3", with_values=False)
     assert bench._algorithmic_bytes(w, q8=True)["q"] == 2 * 16 * 576
     assert bench._algorithmic_bytes(w)["q"] == 2 * 16 * 576 * 2
     pairs = 16 * (100 + 64)
-    want = (2 * 576 * pairs / 5000e12 + 2 * 512 * pairs / 2500e12) * 1e3
+    want = 2 * 1088 * pairs / 5000e12 * 1e3
     assert abs(bench.mfma_floor_ms(w, True) - want) <= 1e-12 * want
     assert abs(bench.mfma_floor_ms(w, False) - 2 * 1088 * pairs / 2500e12 * 1e3) <= 1e-18
 

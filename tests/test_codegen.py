@@ -136,8 +136,8 @@ def _mfma_hazards(instrs):
         op, args = _split(ins)
         if not op.startswith("v_mfma"):
             continue
-        # (1) VALU writes of the sources shortly before
-        srcs = set().union(*(_regs(a) for a in args[1:4]))
+        # (1) VALU writes of the sources (scale registers included) shortly before
+        srcs = set().union(*(_regs(a) for a in args[1:]))
         ws, j = 0, i - 1
         while j >= 0 and ws < VALU_TO_MFMA:
             pop, pargs = _split(instrs[j])
@@ -181,26 +181,67 @@ def decode_asm():
     return _compile("decode.hip")
 
 
-def test_all_kernels_present(decode_asm):
-    """The page kernel in its three instances: bf16 cache, e4m3 cache, e4m3
-    cache with an e4m3 query (whose score MFMAs are the e4m3 ones)."""
+@pytest.fixture(scope="module")
+def q8_asm():
+    return _compile("decode_q8.hip")
+
+
+@pytest.fixture(scope="module")
+def all_bodies(decode_asm, q8_asm):
+    """Every decode kernel body: the page kernel's two instances and the
+    e4m3-query kernel."""
+    bodies = dict(_kernels(decode_asm))
+    bodies.update(_kernels(q8_asm, "mla_decode_q8_kernel"))
+    return bodies
+
+
+def test_all_kernels_present(decode_asm, q8_asm):
+    """The page kernel in its two instances (bf16 cache, e4m3 cache; bf16
+    MFMAs only) and the e4m3-query kernel (e4m3 MFMAs, scaled ones for the
+    output)."""
     bodies = _kernels(decode_asm)
-    assert len(bodies) == 3, list(bodies)
-    f8 = {n: sum("f8f6f4" in i for i in b) for n, b in bodies.items()}
-    assert sorted(f8.values())[:2] == [0, 0] and max(f8.values()) > 0, f8
+    assert len(bodies) == 2, list(bodies)
+    assert all(not any("f8f6f4" in i for i in b) for b in bodies.values())
+    q8 = _kernels(q8_asm, "mla_decode_q8_kernel")
+    assert len(q8) == 1, list(q8)
+    body = next(iter(q8.values()))
+    assert sum("v_mfma_f32_32x32x64_f8f6f4" in i for i in body) > 0
+    assert sum("v_mfma_scale_f32_32x32x64_f8f6f4" in i for i in body) > 0
 
 
-def test_no_instruction_touches_an_in_flight_lds_read(decode_asm):
-    for name, instrs in _kernels(decode_asm).items():
+def test_no_instruction_touches_an_in_flight_lds_read(all_bodies):
+    for name, instrs in all_bodies.items():
         bad = _check(instrs)
         assert not bad, f"{name}: {len(bad)} instructions touch in-flight registers, e.g. {bad[:5]}"
 
 
-def test_decode_kernels_have_no_scratch(decode_asm):
+def test_decode_kernels_have_no_scratch(decode_asm, q8_asm):
     """Every value stays in registers: no VGPR spills and no scratch memory (a
     spill reload would also wait on every page load in flight)."""
-    assert all(int(n) == 0 for n in re.findall(r"\.vgpr_spill_count:\s+(\d+)", decode_asm))
-    assert "scratch_" not in decode_asm
+    for asm in (decode_asm, q8_asm):
+        assert all(int(n) == 0 for n in re.findall(r"\.vgpr_spill_count:\s+(\d+)", asm))
+        assert "scratch_" not in asm
+
+
+def test_q8_output_chain_waits_for_no_page_load(q8_asm):
+    """The e4m3-query kernel's V reads are inline assembly: an LDS read the
+    compiler knew of would get a wait for every page load in flight (vmcnt)
+    in front of it, which puts the next page's load latency into every page.
+    No vmcnt wait may lead into an output chain (its transposing V reads and
+    scaled MFMAs), except the one after a piece's last page, which waits for
+    the next piece's query loads just issued."""
+    body = next(iter(_kernels(q8_asm, "mla_decode_q8_kernel").values()))
+    for i, ins in enumerate(body):
+        if not (ins.startswith("s_waitcnt") and "vmcnt" in ins):
+            continue
+        after = []
+        for x in body[i + 1:i + 41]:
+            if x.startswith("s_barrier"):
+                break
+            after.append(x)
+        leads_in = any("ds_read_b64_tr_b8" in x or "v_mfma_scale" in x for x in after)
+        query_wait = any(x.startswith("global_load") for x in body[max(0, i - 4):i])
+        assert not leads_in or query_wait, (i, body[max(0, i - 4):i + 4])
 
 
 def test_checker_flags_a_planted_use():
@@ -223,8 +264,8 @@ def test_checker_flags_a_planted_use():
     assert _check(smem_drained) == []
 
 
-def test_no_unguarded_mfma_hazard(decode_asm):
-    for name, instrs in _kernels(decode_asm).items():
+def test_no_unguarded_mfma_hazard(all_bodies):
+    for name, instrs in all_bodies.items():
         bad = _mfma_hazards(instrs)
         assert not bad, f"{name}: {len(bad)} MFMA hazards, e.g. {bad[:3]}"
 

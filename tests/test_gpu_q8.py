@@ -86,11 +86,15 @@ def test_q8_non_causal_multi_token(mla):
     assert_close(o, lse, *ref_q8(w, codes, qs))
 
 
-@pytest.mark.parametrize("q_factor", [-1.0, 0.0, 0.25, 3.0])
+@pytest.mark.parametrize("q_factor", [-1.0, 0.0, 0.25, 3.0, 12.0, 40.0])
 def test_q8_query_descale_sign_zero_and_size(mla, q_factor):
     """descale_q enters the scores only: a negative one flips their sign, zero
     weighs every visible key the same.  The codes stay those of the cache
-    scale; only the descale handed to the kernel changes."""
+    scale; only the descale handed to the kernel changes.  Large factors
+    spread the scores over tens to hundreds of log2 units, so later pages'
+    maxima exceed a row's first one by more than the weights' range: those
+    pages take an output scale exponent, and jumps past its limit move the
+    reference max (and rescale the output)."""
     w = make_custom("q8d", bs=2, heads=64, q_len=2, seq_lens=[100, 333], seed=53,
                     kv_dtype="fp8_e4m3", **SMALL)
     qs = _q_scale(w)
