@@ -58,11 +58,13 @@ def _args():
                     help="time replays of the step captured in a HIP graph (measured slower than "
                          "eager launches here: the four launches are not host-bound)")
     ap.add_argument("--cpu-runs", type=int, default=3)
-    ap.add_argument("--plan", choices=("balanced", "fixed"), default="balanced",
+    ap.add_argument("--plan", choices=("balanced", "fixed", "packed"), default="balanced",
                     help="balanced: one cost-balanced part per CU (default); fixed: the "
-                         "deterministic fixed-tile plan (batch-invariant results)")
+                         "deterministic fixed-tile plan, one tile per part; packed: the same "
+                         "tiles packed into one cost-balanced part per CU (batch-invariant "
+                         "results, like fixed)")
     ap.add_argument("--tile-pages", type=int, default=32,
-                    help="pages per tile of the fixed plan (32 = 2048 tokens)")
+                    help="pages per tile of the fixed and packed plans (32 = 2048 tokens)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before warm-up, run one plain elementwise kernel (bitwise not) that "
                          "reads and writes this many MiB: the known-size reference for HBM "
@@ -302,15 +304,16 @@ class Path:
         self.width = w.bt_width
         self.max_len = int(w.seq_lens.max())
         n = mla.device_num_cus()
+        tiles = int(mla._lib.lib().mla_fixed_split_parts_bound(w.bs, self.max_len, tile_pages))
         if plan == "fixed":
-            n = max(1, int(mla._lib.lib().mla_fixed_split_parts_bound(w.bs, self.max_len,
-                                                                     tile_pages)))
+            n = max(1, tiles)
         self.num_parts = n
         dev = "cuda"
         self.bt = torch.empty((w.bs, self.width), dtype=torch.int32, device=dev)
         self.tile_plan = torch.empty((n, 8), dtype=torch.int32, device=dev)
         self.split_indptr = torch.empty((w.bs + 1,), dtype=torch.int32, device=dev)
-        self.po, self.pl = mla.partial_buffers(w.bs, self.R, n)
+        self.po, self.pl = mla.partial_buffers(w.bs, self.R, n,
+                                               num_slots=tiles if plan == "packed" else None)
         self.out = torch.empty((w.bs, w.q_len, w.heads, 512), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((w.bs, w.q_len, w.heads), dtype=torch.float32, device=dev)
         if q8:
@@ -326,6 +329,12 @@ class Path:
             mla.plan_fixed_splits(p.seq_lens, self.tile_pages, self.num_parts,
                                   max_seq_len_hint=self.max_len, tile_plan=self.tile_plan,
                                   split_indptr=self.split_indptr)
+            return
+        if self.plan == "packed":
+            mla.build_block_table(p.req_to_token, p.req_pool_indices, p.seq_lens, self.width,
+                                  max_seq_len_hint=self.max_len, out=self.bt)
+            mla.plan_fixed_packed(p.seq_lens, self.R, self.tile_pages, self.num_parts,
+                                  tile_plan=self.tile_plan, split_indptr=self.split_indptr)
             return
         mla.build_table_and_plan(p.req_to_token, p.req_pool_indices, p.seq_lens, self.width,
                                  self.R, self.num_parts, w.kv_dtype, max_seq_len_hint=self.max_len,
@@ -595,7 +604,9 @@ def main() -> int:
             "seq_len": int(round(float(w.seq_lens.mean()))),
             "parallelism": "single GPU",
             "num_parts": P.num_parts,
-            "plan": a.plan if a.plan == "balanced" else f"fixed tiles of {a.tile_pages} pages",
+            "plan": (a.plan if a.plan == "balanced" else
+                     f"fixed tiles of {a.tile_pages} pages" + (", packed" if a.plan == "packed"
+                                                                else "")),
             "kv_pools_rotated": len(P.pools),
         },
         "pct_hbm_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),

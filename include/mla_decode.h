@@ -198,6 +198,43 @@ mla_status mla_plan_fixed_splits(const int32_t* seq_lens, int32_t bs, int32_t ti
  * -1 for negative sizes or tile_pages <= 0). */
 int32_t mla_fixed_split_parts_bound(int32_t bs, int32_t max_seq_len, int32_t tile_pages);
 /*
+ * mla_plan_fixed_packed — the fixed-size tiles of mla_plan_fixed_splits (the
+ * same pieces: request b is cut at the multiples of tile_pages pages of its
+ * own sequence, and split_indptr is the same), packed into num_parts parts
+ * of about equal cost, as mla_plan_splits packs pages: so a deterministic
+ * plan keeps every CU busy whether the batch has fewer or more tiles than
+ * CUs.  Every tile stays a piece of its own wherever it lands (the decode
+ * ends a piece at each multiple of tile_pages pages of a request, told so
+ * by field 6 of the row), so a request still decodes bit for bit the same
+ * alone or in any batch (FlashInfer backend page, __init__: the
+ * deterministic mode's fixed decode_split_tile_size).
+ *
+ * The rule, in quarter pages: a tile of n pages costs 4 n + c, c the
+ * per-piece overhead of mla_plan_splits for rows_per_req rows; with Q_t the
+ * cost of the tiles before tile t (request order, then tile order), C the
+ * total and x_p = floor(p C / num_parts), part p holds the tiles from the
+ * boundary whose Q is nearest x_p (the lower one on a tie) to that of
+ * x_{p+1} (part num_parts - 1 ends at the last tile).  Row p is
+ *   {first request, its first page, last request, end page there,
+ *    tile index of the first tile in its request, pages, tile_pages, 0}
+ * (all zeros for an empty part).  Every part costs at most C / num_parts
+ * plus one tile.
+ *
+ * Pass the plan to mla_decode with num_parts and partial_slots >= the
+ * number of tiles, split_indptr[bs] (at most mla_fixed_split_parts_bound).
+ *
+ *   tile_plan     int32 [num_parts, 8], 16-byte aligned
+ *   split_indptr  int32 [bs + 1]
+ *
+ * Errors: INVALID_ARGUMENT for null pointers or bs, tile_pages, num_parts
+ * <= 0; UNSUPPORTED for rows_per_req outside 1..512 or a misaligned
+ * tile_plan; CAPACITY for bs > MLA_MAX_BATCH or num_parts above the CU count
+ * (or MLA_MAX_PARTS).  The total cost must stay below 2^31 quarter pages.
+ */
+mla_status mla_plan_fixed_packed(const int32_t* seq_lens, int32_t bs, int32_t tile_pages,
+                                 int32_t rows_per_req, int32_t num_parts, int32_t* tile_plan,
+                                 int32_t* split_indptr, hipStream_t stream);
+/*
  * mla_build_table_and_plan — mla_build_block_table and mla_plan_splits in
  * one launch (init_forward_metadata of both page backends computes the block
  * table and the split metadata together, once per batch step).  One work-group

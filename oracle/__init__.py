@@ -25,4 +25,6 @@ from .paged_mla import (  # noqa: F401
     merge_states,
 )
 from .kv_append import e4m3fn_encode, quantize_rows, quantize_q, set_kv_buffer  # noqa: F401
-from .plan import plan_reference, check_plan, plan_overhead, plan_fixed, check_fixed_plan  # noqa: F401
+from .plan import (  # noqa: F401
+    plan_reference, check_plan, plan_overhead, plan_fixed, check_fixed_plan, plan_fixed_packed,
+    check_fixed_packed_plan)

@@ -214,3 +214,107 @@ def check_fixed_plan(table, indptr, seq_lens, tile_pages: int) -> None:
             covered = pg1
         assert covered == npages[b]
     assert not np.any(table[int(indptr[-1]):])
+
+
+# ------------------------------------------------------------ packed fixed-size tiles
+
+def plan_fixed_packed(seq_lens, tile_pages: int, num_parts: int, rows_per_req: int):
+    """The fixed-size tiles of :func:`plan_fixed` (the same pieces, the same
+    split_indptr), packed into ``num_parts`` contiguous parts of about equal
+    cost, so that a batch whose tiles outnumber or undercut the CUs keeps
+    every CU busy.  A tile stays a piece of its own wherever it lands, so a
+    request still decodes bit for bit the same in any batch.
+
+    The rule, in quarter pages: tile t (in request order, then tile order)
+    costs 4 n_t + c, n_t its pages, c = plan_overhead(rows_per_req); Q_t is
+    the cost of the tiles before t (Q_0 = 0, Q_NT = C).  With
+    x_p = floor(p C / num_parts), cut p is the tile boundary t whose Q_t is
+    nearest x_p (the lower one on a tie); part p holds tiles [cut_p, cut_p+1).
+
+    Table row: (first request, its first page, last request, end page in the
+    last request, piece index of the first tile in its request, pages,
+    tile_pages, 0); an empty part is all zeros.  Field 6 tells the decode to
+    end a piece at every multiple of tile_pages pages of a request.
+    """
+    L = np.asarray(seq_lens, dtype=np.int64)
+    bs = len(L)
+    T = int(tile_pages)
+    c = plan_overhead(rows_per_req)
+    npages = -(-L // PAGE_SIZE)
+    tiles = []  # (request, tile index, first page, end page)
+    for b in range(bs):
+        n = int(npages[b])
+        for k in range(-(-n // T)):
+            tiles.append((b, k, k * T, min((k + 1) * T, n)))
+    pieces = np.array([-(-int(n) // T) for n in npages], dtype=np.int64)
+    indptr = np.concatenate([[0], np.cumsum(pieces)]).astype(np.int32)
+    Q = [0]
+    for (_, _, pg0, pg1) in tiles:
+        Q.append(Q[-1] + 4 * (pg1 - pg0) + c)
+    C = Q[-1]
+    NT = len(tiles)
+
+    def nearest(x: int) -> int:
+        best = 0
+        for t in range(NT + 1):
+            if abs(Q[t] - x) < abs(Q[best] - x):
+                best = t
+        return best
+
+    cuts = [nearest(p * C // num_parts) for p in range(num_parts)] + [NT]
+    cuts[0] = 0
+    table = np.zeros((num_parts, 8), dtype=np.int32)
+    for p in range(num_parts):
+        t0, t1 = cuts[p], cuts[p + 1]
+        if t1 <= t0:
+            continue
+        b0, k0, pg0, _ = tiles[t0]
+        b1, _, _, pg1 = tiles[t1 - 1]
+        pages = sum(e - s for (_, _, s, e) in tiles[t0:t1])
+        table[p] = (b0, pg0, b1, pg1, k0, pages, T, 0)
+    return table, indptr
+
+
+def check_fixed_packed_plan(table, indptr, seq_lens, tile_pages: int, num_parts: int,
+                            rows_per_req: int) -> None:
+    """Raise AssertionError unless (table, indptr) is a packed fixed-tile plan:
+    split_indptr is that of :func:`plan_fixed` (one piece per tile); the parts
+    cover the (request, page) sequence in order, each page exactly once, and
+    start and end on tile boundaries; field 4 is the first tile's index in
+    its request, field 6 the tile size; and every part costs at most
+    ceil(C / num_parts) plus one tile's cost (4 tile_pages + c)."""
+    table = np.asarray(table)
+    indptr = np.asarray(indptr, dtype=np.int64)
+    L = np.asarray(seq_lens, dtype=np.int64)
+    T = int(tile_pages)
+    c = plan_overhead(rows_per_req)
+    npages = -(-L // PAGE_SIZE)
+    _, ref_indptr = plan_fixed(L, T, 1 << 30)
+    assert np.array_equal(indptr, ref_indptr)
+    assert table.shape == (num_parts, 8)
+    C = int(sum(4 * int(n) + c * (-(-int(n) // T)) for n in npages))
+    bound = -(-C // num_parts) + 4 * T + c
+    seen = [np.zeros(int(n), dtype=np.int64) for n in npages]
+    last = (0, 0)
+    for p in range(num_parts):
+        b0, pg0, b1, pg1, k0, npg, tc, r1 = [int(v) for v in table[p]]
+        if npg == 0:
+            assert not np.any(table[p]), table[p]
+            continue
+        assert tc == T and r1 == 0 and 0 <= b0 <= b1 < len(L), table[p]
+        assert (b0, pg0) >= last, f"part {p} out of order"
+        assert pg0 % T == 0 and k0 == pg0 // T, table[p]
+        assert pg1 == npages[b1] or pg1 % T == 0, table[p]
+        count = cost = 0
+        for b in range(b0, b1 + 1):
+            lo = pg0 if b == b0 else 0
+            hi = pg1 if b == b1 else int(npages[b])
+            assert 0 <= lo <= hi <= npages[b], table[p]
+            seen[b][lo:hi] += 1
+            count += hi - lo
+            cost += 4 * (hi - lo) + c * len(range(lo // T, -(-hi // T))) if hi > lo else 0
+        assert count == npg, table[p]
+        assert cost <= bound, f"part {p} cost {cost} > {bound}"
+        last = (b1, pg1)
+    for b in range(len(L)):
+        assert np.all(seen[b] == 1), f"request {b} pages not covered exactly once"

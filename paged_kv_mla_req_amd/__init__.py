@@ -173,6 +173,43 @@ def plan_fixed_splits(seq_lens: torch.Tensor, tile_pages: int = 32,
     return tile_plan, split_indptr
 
 
+def plan_fixed_packed(seq_lens: torch.Tensor, rows_per_req: int, tile_pages: int = 32,
+                      num_parts: Optional[int] = None,
+                      tile_plan: Optional[torch.Tensor] = None,
+                      split_indptr: Optional[torch.Tensor] = None,
+                      stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The fixed tiles of plan_fixed_splits packed into ``num_parts`` parts of
+    about equal cost (mla_plan_fixed_packed; default: one per CU).  The decode
+    needs partial slots for every tile: size its workspace with
+    partial_buffers(..., num_slots=split_indptr[bs]) or an upper bound
+    (fixed_split_parts_bound).  Returns (tile_plan int32 [num_parts, 8],
+    split_indptr int32 [bs + 1])."""
+    _need(seq_lens, "seq_lens", (torch.int32,), 1)
+    bs = seq_lens.shape[0]
+    if num_parts is None:
+        num_parts = device_num_cus()
+    if tile_plan is None:
+        tile_plan = torch.empty((num_parts, 8), dtype=torch.int32, device=seq_lens.device)
+    if split_indptr is None:
+        split_indptr = torch.empty((bs + 1,), dtype=torch.int32, device=seq_lens.device)
+    _need(tile_plan, "tile_plan", (torch.int32,), 2)
+    _need(split_indptr, "split_indptr", (torch.int32,), 1)
+    if tile_plan.shape != (num_parts, 8) or split_indptr.shape != (bs + 1,):
+        raise ValueError("tile_plan must be [num_parts, 8] and split_indptr [bs + 1]")
+    _same_device(("seq_lens", seq_lens), ("tile_plan", tile_plan),
+                 ("split_indptr", split_indptr))
+    _lib.check(_lib.lib().mla_plan_fixed_packed(_p(seq_lens), bs, tile_pages, rows_per_req,
+                                                num_parts, _p(tile_plan), _p(split_indptr),
+                                                _stream(stream)))
+    return tile_plan, split_indptr
+
+
+def fixed_split_parts_bound(bs: int, max_seq_len: int, tile_pages: int = 32) -> int:
+    """Most tiles (pieces) a fixed-tile plan of bs requests of up to
+    max_seq_len tokens can have (mla_fixed_split_parts_bound)."""
+    return int(_lib.lib().mla_fixed_split_parts_bound(bs, max_seq_len, tile_pages))
+
+
 def build_table_and_plan(req_to_token: torch.Tensor, req_pool_indices: torch.Tensor,
                          seq_lens: torch.Tensor, width: int, rows_per_req: int,
                          num_parts: Optional[int] = None, kv_dtype="bf16", pad_value: int = -1,
@@ -215,11 +252,14 @@ def build_table_and_plan(req_to_token: torch.Tensor, req_pool_indices: torch.Ten
     return out, tile_plan[:num_parts], split_indptr[:bs + 1]
 
 
-def partial_buffers(bs: int, rows_per_req: int, num_parts: int,
-                    device="cuda") -> Tuple[torch.Tensor, torch.Tensor]:
-    """Workspace for split pieces: partial o bf16 [bs+num_parts, R, 512] and
-    partial lse fp32 [bs+num_parts, R]."""
+def partial_buffers(bs: int, rows_per_req: int, num_parts: int, device="cuda",
+                    num_slots: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Workspace for split pieces: partial o bf16 [S, R, 512] and partial lse
+    fp32 [S, R], S = bs + num_parts (the most pieces of a balanced plan), or
+    at least ``num_slots`` (a fixed-tile plan: its number of tiles)."""
     slots = max_total_splits(bs, num_parts)
+    if num_slots is not None:
+        slots = max(slots, int(num_slots))
     return (torch.empty((slots, rows_per_req, V_DIM), dtype=torch.bfloat16, device=device),
             torch.empty((slots, rows_per_req), dtype=torch.float32, device=device))
 

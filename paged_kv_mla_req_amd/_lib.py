@@ -38,6 +38,7 @@ SIGNATURES = {
                                           _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_p,
                                           _c_p, _c_p]),
     "mla_plan_fixed_splits": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_p, _c_p]),
+    "mla_plan_fixed_packed": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_p, _c_p]),
     "mla_fixed_split_parts_bound": (_c_i32, [_c_i32, _c_i32, _c_i32]),
     "mla_max_total_splits": (_c_i32, [_c_i32, _c_i32]),
     "mla_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32]),

@@ -80,6 +80,10 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
   const int32_t* tp = tile_plan + part * 8;
   const int b_first = tp[0], pg_first = tp[1], b_last = tp[2], pg_last = tp[3];
   const int first_piece = tp[4], total = tp[5];
+  // pieces also end at the multiples of tile_cut pages of a request (a packed
+  // fixed-tile plan: several tiles of one request in one part are pieces of
+  // their own); 0: only where a request ends
+  const int tile_cut = tp[6];
   // An empty part, or a row no planner would produce, does nothing (the
   // check is uniform over the work-group, so no wave is left at a barrier).
   if (total <= 0 || b_first < 0 || b_last >= P.bs || b_first > b_last || pg_first < 0 ||
@@ -239,7 +243,10 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
   while (true) {
     // ---- one piece: pages [cp, cend) of request cb ---------------------------
     const int32_t L = uniform_load(seq_lens, cb);
-    const int cend = (cb == b_last) ? pg_last : page_count(L);
+    const int req_end = (cb == b_last) ? pg_last : page_count(L);
+    const int cend = tile_cut > 0 ? min(req_end, (cp / tile_cut + 1) * tile_cut) : req_end;
+    // the next piece is the next tile of this request (same queries)
+    const bool same_next = cend < req_end;
     // pages from first_masked on may hold keys some row of this wave cannot see
     const int32_t lim_min = P.causal ? L - P.q_len + i_tok_min : L - 1;
     const int first_masked =
@@ -257,7 +264,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
     // would otherwise wait for them at the score MFMAs of every page, behind
     // the next page's loads issued there)
     auto prefetch_q = [&]() {
-      if (cp + 1 == cend && it + 1 < total && cb < b_last) {
+      if (cp + 1 == cend && it + 1 < total && cb < b_last && !same_next) {
         load_q(ncb);
         __builtin_amdgcn_s_waitcnt(0x0f70);
       }
@@ -491,7 +498,7 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
     for (; cp < cend && it < total; ++cp, ++it) page(std::true_type{});
 
     // ---- epilogue of the piece ---------------------------------------------------
-    const bool more = it < total && cb < b_last;
+    const bool more = it < total && (cb < b_last || same_next);
     if (more) {
       // the next piece's queries and first page land before any store goes out
       __builtin_amdgcn_s_waitcnt(0x0f70);
@@ -528,9 +535,13 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
     }
     if (!more) break;
     park_offsets();
-    cb = ncb;
-    cp = 0;
-    piece = 0;
+    if (same_next) {
+      ++piece;
+    } else {
+      cb = ncb;
+      cp = 0;
+      piece = 0;
+    }
   }
   // Only reached early with a malformed plan: keep the barrier count.
   for (; it < total; ++it) {

@@ -382,6 +382,9 @@ mla_decode_q8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ 
   const int32_t* tp = tile_plan + part * 8;
   const int b_first = tp[0], pg_first = tp[1], b_last = tp[2], pg_last = tp[3];
   const int first_piece = tp[4], total = tp[5];
+  // pieces also end at the multiples of tile_cut pages of a request (packed
+  // fixed-tile plan); 0: only where a request ends
+  const int tile_cut = tp[6];
   if (total <= 0 || b_first < 0 || b_last >= P.bs || b_first > b_last || pg_first < 0 ||
       first_piece < 0)
     return;
@@ -480,7 +483,11 @@ mla_decode_q8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ 
   // score side: the page `it` (request cb, page cp of it, piece `piece`)
   int cb = b_first, cp = pg_first, piece = first_piece;
   int32_t L = uniform_load(seq_lens, cb);
-  int cend = (cb == b_last) ? pg_last : page_count(L);
+  int req_end = (cb == b_last) ? pg_last : page_count(L);
+  auto tile_end = [&](int page) {
+    return tile_cut > 0 ? min(req_end, (page / tile_cut + 1) * tile_cut) : req_end;
+  };
+  int cend = tile_end(cp);
   auto first_masked_of = [&](int32_t len) {
     const int32_t lim_min = P.causal ? len - P.q_len + i_tok_min : len - 1;
     return __builtin_amdgcn_readfirstlane(lim_min >= 0 ? (lim_min + 1) / kPage : 0);
@@ -546,7 +553,7 @@ mla_decode_q8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ 
       score_chain8(sc0, sc1, qreg, ka, hook, NoSlot{});
       // the piece's last page: its queries are no longer needed; load the next
       // piece's (waited for here, with the next page's loads)
-      if (cp + 1 == cend && it + 1 < total && cb < b_last) {
+      if (cp + 1 == cend && it + 1 < total && cb < b_last && cend == req_end) {
         int ncb = cb;
         do {
           ++ncb;
@@ -684,16 +691,24 @@ mla_decode_q8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ 
         pv_l = l_run;
         m_ref = -INFINITY;
         l_run = 0.f;
-        if (cb < b_last) {
-          do {
-            ++cb;
-            L = uniform_load(seq_lens, cb);
-          } while (cb < b_last && page_count(L) <= 0);
-          cend = (cb == b_last) ? pg_last : page_count(L);
-          first_masked = first_masked_of(L);
+        if (cend < req_end) {
+          // the next tile of the same request (same queries)
+          ++cp;
+          ++piece;
+          cend = tile_end(cp);
+        } else {
+          if (cb < b_last) {
+            do {
+              ++cb;
+              L = uniform_load(seq_lens, cb);
+            } while (cb < b_last && page_count(L) <= 0);
+            req_end = (cb == b_last) ? pg_last : page_count(L);
+            first_masked = first_masked_of(L);
+          }
+          cp = 0;
+          piece = 0;
+          cend = tile_end(cp);
         }
-        cp = 0;
-        piece = 0;
       } else {
         ++cp;
       }

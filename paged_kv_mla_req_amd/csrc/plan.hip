@@ -591,6 +591,104 @@ __global__ __launch_bounds__(kPlanThreads) void plan_fixed_kernel(
     tile_plan[i] = 0;
 }
 
+// Packed fixed-tile plan: the tiles of plan_fixed_kernel (the same pieces and
+// split_indptr), in request order, cut into `parts` contiguous runs of about
+// equal cost.  In quarter pages a tile of n pages costs 4 n + overhead; with
+// Q_t the cost before tile t and x_p = floor(p C / parts), cut p is the tile
+// boundary whose Q_t is nearest x_p (the lower one on a tie).  Each thread
+// finds its cuts by one binary search over the requests' cost prefix and a
+// division inside the request (its tiles but the last cost the same); the
+// row then needs the requests of its first and last tile.
+// LDS: 2 (bs + 1) + parts + 1 + kPlanWaves ints.
+__global__ __launch_bounds__(kPlanThreads) void plan_fixed_packed_kernel(
+    const int32_t* __restrict__ seq_lens, int32_t bs, int32_t tile_pages, int32_t overhead,
+    int32_t parts, int32_t* __restrict__ tile_plan, int32_t* __restrict__ split_indptr) {
+  extern __shared__ int smem[];
+  int* tpre = smem;                    // [bs + 1] tiles before request b
+  int* cpre = tpre + (bs + 1);         // [bs + 1] cost before request b
+  int* cuts = cpre + (bs + 1);         // [parts + 1] first tile of part p
+  int* wave_tot = cuts + (parts + 1);  // [kPlanWaves]
+  const int t = threadIdx.x, T = tile_pages;
+  const int chunk = (bs + kPlanThreads - 1) / kPlanThreads;
+  const int b_begin = min(bs, t * chunk);
+  const int b_end = min(bs, b_begin + chunk);
+
+  // 1. tiles and cost per request, prefix sums; split_indptr = tile prefix
+  int my_tiles = 0, my_cost = 0;
+  for (int b = b_begin; b < b_end; ++b) {
+    const int32_t L = seq_lens[b];
+    const int np = L > 0 ? (L >> 6) + ((L & (kPage - 1)) != 0) : 0;
+    const int n = np / T + (np % T != 0);
+    tpre[b] = n;
+    cpre[b] = 4 * np + overhead * n;
+    my_tiles += n;
+    my_cost += 4 * np + overhead * n;
+  }
+  int NT, C;
+  int toff = block_exclusive_scan(my_tiles, wave_tot, &NT);
+  int coff = block_exclusive_scan(my_cost, wave_tot, &C);
+  for (int b = b_begin; b < b_end; ++b) {
+    const int n = tpre[b], c = cpre[b];
+    tpre[b] = toff;
+    cpre[b] = coff;
+    split_indptr[b] = toff;
+    toff += n;
+    coff += c;
+  }
+  if (t == 0) {
+    tpre[bs] = NT;
+    cpre[bs] = C;
+    split_indptr[bs] = NT;
+  }
+  __syncthreads();
+
+  // 2. cuts: the tile boundary nearest each cost position
+  const int w = 4 * T + overhead;  // cost of every tile of a request but its last
+  for (int p = t; p <= parts; p += kPlanThreads) {
+    int cut = NT;
+    const int64_t x64 = (int64_t)p * C / parts;
+    if (p == 0) {
+      cut = 0;
+    } else if (p < parts && x64 < C) {
+      const int x = (int)x64;
+      const int b = upper_bound(cpre, bs, x) - 1;  // cpre[b] <= x < cpre[b + 1]
+      const int o = x - cpre[b];
+      const int n = tpre[b + 1] - tpre[b];
+      const int k0 = min(o / w, n - 1);
+      const int q0 = k0 * w;
+      const int q1 = k0 + 1 < n ? (k0 + 1) * w : cpre[b + 1] - cpre[b];
+      cut = tpre[b] + (o - q0 <= q1 - o ? k0 : k0 + 1);
+    }
+    cuts[p] = cut;
+  }
+  __syncthreads();
+
+  // 3. one row per part
+  auto pages_before = [&](int b) { return (cpre[b] - overhead * tpre[b]) >> 2; };
+  for (int p = t; p < parts; p += kPlanThreads) {
+    int row[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    const int t0 = cuts[p], t1 = cuts[p + 1];
+    if (t1 > t0) {
+      const int b0 = upper_bound(tpre, bs, t0) - 1;
+      const int k0 = t0 - tpre[b0];
+      const int b1 = upper_bound(tpre, bs, t1 - 1) - 1;
+      const int k1 = t1 - 1 - tpre[b1];
+      const int np1 = pages_before(b1 + 1) - pages_before(b1);
+      const int pg1 = min((k1 + 1) * T, np1);
+      row[0] = b0;
+      row[1] = k0 * T;
+      row[2] = b1;
+      row[3] = pg1;
+      row[4] = k0;
+      row[5] = (pages_before(b1) + pg1) - (pages_before(b0) + k0 * T);
+      row[6] = T;
+    }
+    int4* dst = reinterpret_cast<int4*>(tile_plan + p * 8);
+    dst[0] = make_int4(row[0], row[1], row[2], row[3]);
+    dst[1] = make_int4(row[4], row[5], row[6], row[7]);
+  }
+}
+
 // ceil(ceil(max_seq_len / 64) / tile_pages) pieces per request, times bs;
 // -1 for bad arguments, INT32_MAX when the count does not fit.
 int64_t fixed_parts_bound(int32_t bs, int32_t max_seq_len, int32_t tile_pages) {
@@ -632,4 +730,28 @@ extern "C" mla_status mla_plan_fixed_splits(const int32_t* seq_lens, int32_t bs,
   hipLaunchKernelGGL(plan_fixed_kernel, dim3(1), dim3(kPlanThreads), 0, stream, seq_lens, bs,
                      tile_pages, max_parts, tile_plan, split_indptr);
   return check_launch(w.c_str());
+}
+
+extern "C" mla_status mla_plan_fixed_packed(const int32_t* seq_lens, int32_t bs,
+                                            int32_t tile_pages, int32_t rows_per_req,
+                                            int32_t num_parts, int32_t* tile_plan,
+                                            int32_t* split_indptr, hipStream_t stream) {
+  using namespace mla;
+  const char* who = "mla_plan_fixed_packed";
+  const std::string w(who);
+  if (tile_pages <= 0)
+    return fail(MLA_ERR_INVALID_ARGUMENT, w + ": tile_pages must be positive");
+  const mla_status st = check_plan_args(who, seq_lens, bs, rows_per_req, num_parts, MLA_KV_BF16,
+                                        tile_plan, split_indptr);
+  if (st != MLA_OK) return st;
+  const size_t lds = sizeof(int) * (2 * (size_t)(bs + 1) + (size_t)num_parts + 1 + kPlanWaves);
+  static std::atomic<bool> lds_raised[kMaxDevices];
+  const mla_status la = allow_plan_lds(plan_fixed_packed_kernel, lds_raised, who);
+  if (la != MLA_OK) return la;
+  trace("%s: bs %d tile_pages %d rows %d parts %d lds %zu stream %p", who, bs, tile_pages,
+        rows_per_req, num_parts, lds, (void*)stream);
+  hipLaunchKernelGGL(plan_fixed_packed_kernel, dim3(1), dim3(kPlanThreads), lds, stream, seq_lens,
+                     bs, tile_pages, plan_overhead_q(rows_per_req), num_parts, tile_plan,
+                     split_indptr);
+  return check_launch(who);
 }

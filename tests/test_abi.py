@@ -206,6 +206,23 @@ def test_fixed_plan_argument_errors_and_bound():
     assert b(16384, 2**31 - 1, 1) == 2**31 - 1
 
 
+def test_fixed_packed_plan_argument_errors():
+    lib = _lib.lib()
+    f = lib.mla_plan_fixed_packed  # (seq_lens, bs, tile_pages, rows, parts, tile_plan, indptr, stream)
+    assert f(None, 2, 32, 128, 8, FAKE, FAKE, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert f(FAKE, 2, 32, 128, 8, None, FAKE, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert f(FAKE, 0, 32, 128, 8, FAKE, FAKE, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert f(FAKE, 2, 0, 128, 8, FAKE, FAKE, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert f(FAKE, 2, -3, 128, 8, FAKE, FAKE, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert f(FAKE, 2, 32, 128, 0, FAKE, FAKE, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert f(FAKE, 2, 32, 0, 8, FAKE, FAKE, None) == _lib.MLA_ERR_UNSUPPORTED
+    assert f(FAKE, 2, 32, 513, 8, FAKE, FAKE, None) == _lib.MLA_ERR_UNSUPPORTED
+    assert f(FAKE, 2, 32, 128, 8, P(0x1004), FAKE, None) == _lib.MLA_ERR_UNSUPPORTED
+    assert f(FAKE, 20000, 32, 128, 8, FAKE, FAKE, None) == _lib.MLA_ERR_CAPACITY
+    assert f(FAKE, 2, 32, 128, 65537, FAKE, FAKE, None) == _lib.MLA_ERR_CAPACITY
+    assert lib.mla_last_error_message().startswith(b"mla_plan_fixed_packed")
+
+
 def test_quantize_q_argument_errors():
     f = _lib.lib().mla_quantize_q_fp8
     assert f(None, 576, 4, FAKE, FAKE, None) == _lib.MLA_ERR_INVALID_ARGUMENT

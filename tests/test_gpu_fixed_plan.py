@@ -195,3 +195,117 @@ def test_fixed_plan_decode_with_empty_and_one_token_requests(mla):
     assert_close(o, l, o_ref, lse_ref)
     for b in (0, 3):
         assert np.all(o[b] == 0) and np.all(l[b] == -np.inf)
+
+
+# ------------------------------------------------------------ packed fixed tiles
+
+@pytest.mark.parametrize("lens,T,parts,rows", [
+    ([37, 130], 1, 4, 16), ([0], 32, 3, 128), ([1], 32, 256, 128), ([0, 5, 0, 700], 4, 7, 64),
+    ([130, 64, 300, 4000], 8, 5, 128), ("dsv3", 32, 256, 128), ("dsv3", 16, 256, 128),
+    ("long", 32, 256, 128), ("verify", 16, 256, 64), ("fp8", 32, 256, 128),
+    ("rand1000", 16, 200, 128), ("many16384", 32, 256, 16),
+])
+def test_fixed_packed_plan_bit_exact(mla, lens, T, parts, rows):
+    if lens == "rand1000":
+        lens = np.random.default_rng(3).integers(0, 20000, size=1000)
+    elif lens == "many16384":
+        lens = np.random.default_rng(4).integers(1, 200, size=16384)
+    elif isinstance(lens, str):
+        lens = workload_seq_lens(lens)
+    lens = np.asarray(lens, dtype=np.int32)
+    parts = min(parts, mla.device_num_cus())
+    sl = torch.from_numpy(lens).cuda()
+    t, ip = mla.plan_fixed_packed(sl, rows, T, parts)
+    t_ref, ip_ref = oracle.plan_fixed_packed(lens, T, parts, rows)
+    assert np.array_equal(_np(ip), ip_ref)
+    assert np.array_equal(_np(t), t_ref)
+    oracle.check_fixed_packed_plan(_np(t), _np(ip), lens, T, parts, rows)
+
+
+def _packed_decode(mla, d, w, bt_width, T, parts, idx=None, q8=False):
+    q, sl, rpi = d.q, d.seq_lens, d.req_pool_indices
+    if idx is not None:
+        ii = torch.as_tensor(idx, dtype=torch.long, device="cuda")
+        q, sl, rpi = q[ii].contiguous(), sl[ii].contiguous(), rpi[ii].contiguous()
+    bt = mla.build_block_table(d.req_to_token, rpi, sl, bt_width)
+    plan = mla.plan_fixed_packed(sl, w.rows_per_req, T, parts)
+    tiles = int(_np(plan[1])[-1])
+    ws = mla.partial_buffers(sl.shape[0], w.rows_per_req, parts, num_slots=tiles)
+    kw = {}
+    if q8:
+        qs = float(np.float32(w.kv_descale))
+        kw["q_descale"] = torch.tensor([qs], dtype=torch.float32, device="cuda")
+        q = torch.from_numpy(oracle.quantize_q(w.q_bits, qs)).cuda()
+        if idx is not None:
+            q = q[ii].contiguous()
+    out, lse = mla.decode(q, d.kv, bt, sl, w.softmax_scale, kv_dtype=w.kv_dtype,
+                          kv_descale=d.kv_descale, causal=w.causal, plan=plan, workspace=ws,
+                          **kw)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+PACKED_CASES = [
+    dict(bs=2, heads=16, q_len=1, lens=[37, 130], T=1, parts=2, kv="bf16"),
+    dict(bs=6, heads=128, q_len=1, lens=[100, 3000, 5000, 64, 2049, 777], T=4, parts=7, kv="bf16"),
+    dict(bs=4, heads=16, q_len=4, lens=[5, 300, 1500, 4100], T=2, parts=9, kv="bf16"),
+    dict(bs=3, heads=128, q_len=1, lens=[129, 2500, 4096], T=8, parts=3, kv="fp8_e4m3"),
+    dict(bs=5, heads=20, q_len=1, lens=[64, 1, 900, 3, 2000], T=3, parts=4, kv="bf16"),
+]
+
+
+@pytest.mark.parametrize("c", PACKED_CASES,
+                         ids=lambda c: f"b{c['bs']}h{c['heads']}n{c['q_len']}T{c['T']}P{c['parts']}{c['kv']}")
+def test_fixed_packed_decode_matches_oracle(mla, c):
+    """Parts holding several tiles, of one request or of several: each tile
+    a piece of its own, every row at the bar."""
+    w = make_custom("packed", bs=c["bs"], heads=c["heads"], q_len=c["q_len"], seq_lens=c["lens"],
+                    seed=44, kv_dtype=c["kv"], value_scale=0.5)
+    d = to_device(w)
+    out, lse = _packed_decode(mla, d, w, w.bt_width, c["T"], c["parts"])
+    assert_close(_np(out), _np(lse), *ref(w))
+
+
+def test_fixed_packed_q8_decode_matches_oracle(mla):
+    from tests.test_gpu_q8 import ref_q8
+    w = make_custom("packed8", bs=4, heads=128, q_len=1, seq_lens=[700, 64, 3000, 1290], seed=45,
+                    kv_dtype="fp8_e4m3")
+    d = to_device(w)
+    qs = float(np.float32(w.kv_descale))
+    out, lse = _packed_decode(mla, d, w, w.bt_width, 5, 6, q8=True)
+    assert_close(_np(out), _np(lse), *ref_q8(w, oracle.quantize_q(w.q_bits, qs), qs))
+
+
+@pytest.mark.parametrize("q8", [False, True])
+def test_fixed_packed_batch_invariance_bit_exact(mla, q8):
+    """A request gives the same bits packed with others (whatever part its
+    tiles land in), in a reordered sub-batch with another part count, and
+    alone -- and the same bits as the one-tile-per-part fixed plan."""
+    lens = [100, 3000, 5000, 64, 2049, 777, 4097, 1]
+    kv = "fp8_e4m3" if q8 else "bf16"
+    w = make_custom("pinv", bs=len(lens), heads=128, q_len=1, seq_lens=lens, seed=46,
+                    value_scale=0.5, kv_dtype=kv)
+    d = to_device(w)
+    T = 4
+    out_a, lse_a = _packed_decode(mla, d, w, w.bt_width, T, 13, q8=q8)
+    idx = [6, 1, 2, 4]
+    out_b, lse_b = _packed_decode(mla, d, w, w.bt_width + 3, T, 5, idx=idx, q8=q8)
+    ii = torch.as_tensor(idx, device="cuda")
+    assert torch.equal(out_b.view(torch.int16), out_a[ii].view(torch.int16))
+    assert torch.equal(lse_b, lse_a[ii])
+    for i in idx:
+        out_c, lse_c = _packed_decode(mla, d, w, w.bt_width, T, 3, idx=[i], q8=q8)
+        assert torch.equal(out_c.view(torch.int16), out_a[i:i + 1].view(torch.int16))
+        assert torch.equal(lse_c, lse_a[i:i + 1])
+    if not q8:
+        out_f, lse_f = _fixed_decode(mla, d, w, w.bt_width, T, _need(lens, T))
+        assert torch.equal(out_f.view(torch.int16), out_a.view(torch.int16))
+        assert torch.equal(lse_f, lse_a)
+
+
+@pytest.mark.parametrize("name,T", [("dsv3", 16), ("dsv3", 32), ("verify", 16), ("fp8", 32)])
+def test_fixed_packed_full_size_all_rows(mla, name, T):
+    w = make_workload(name)
+    d = to_device(w)
+    out, lse = _packed_decode(mla, d, w, w.bt_width, T, mla.device_num_cus())
+    assert_close(_np(out), _np(lse), *ref(w))

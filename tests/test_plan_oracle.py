@@ -129,3 +129,86 @@ def test_fixed_plan_overflow_plans_nothing_and_checker_catches_mutations():
         mutate(bad)
         with pytest.raises(AssertionError):
             oracle.check_fixed_plan(bad, ip, lens, 4)
+
+
+# ------------------------------------------------------------ packed fixed tiles
+
+def test_fixed_packed_plan_worked_example():
+    """Hand-worked case.  L = [130, 64, 300, 4000], T = 8, 128 rows (c = 12
+    quarter pages), 5 parts.  Pages 3, 1, 5, 63; tiles: one each for the first
+    three requests (costs 24, 16, 32), eight for the last (seven of 8 pages,
+    cost 44 each, and one of 7, cost 40).  Boundaries Q = 0, 24, 40, 72, 116,
+    160, 204, 248, 292, 336, 380, 420 (C = 420); positions x_p = 0, 84, 168,
+    252, 336 pick boundaries 72 (t = 3), 160 (t = 5), 248 (t = 7), 336 (t = 9)."""
+    t, ip = oracle.plan_fixed_packed([130, 64, 300, 4000], 8, 5, 128)
+    assert ip.tolist() == [0, 1, 2, 3, 11]
+    assert t.tolist() == [[0, 0, 2, 5, 0, 9, 8, 0],
+                          [3, 0, 3, 16, 0, 16, 8, 0],
+                          [3, 16, 3, 32, 2, 16, 8, 0],
+                          [3, 32, 3, 48, 4, 16, 8, 0],
+                          [3, 48, 3, 63, 6, 15, 8, 0]]
+
+
+def test_fixed_packed_plan_tie_goes_to_the_lower_boundary():
+    """Two requests of one 1-page tile each, 32 rows (c = 6 quarter pages):
+    each tile costs 10, Q = 0, 10, 20, C = 20.  With 4 parts the positions
+    5 and 15 sit exactly between two boundaries and take the lower one (0 and
+    10), so parts 0 and 2 stay empty."""
+    assert oracle.plan_overhead(32) == 6
+    t, ip = oracle.plan_fixed_packed([10, 20], 4, 4, 32)
+    assert ip.tolist() == [0, 1, 2]
+    assert t.tolist() == [[0] * 8, [0, 0, 0, 1, 0, 1, 4, 0], [0] * 8, [1, 0, 1, 1, 0, 1, 4, 0]]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_fixed_packed_plan_random_batches_are_valid(seed):
+    rng = np.random.default_rng(100 + seed)
+    for _ in range(40):
+        bs = int(rng.integers(1, 60))
+        L = rng.integers(0, 9000, size=bs)
+        L[rng.random(bs) < 0.2] = 0
+        T = int(rng.integers(1, 48))
+        P = int(rng.integers(1, 300))
+        R = int(rng.choice([1, 16, 64, 128, 512]))
+        t, ip = oracle.plan_fixed_packed(L, T, P, R)
+        oracle.check_fixed_packed_plan(t, ip, L, T, P, R)
+
+
+def test_fixed_packed_plan_keeps_the_fixed_plan_pieces():
+    """Packing changes which part holds a tile, never the tiles: with one
+    part per tile and equal tile costs every part holds one tile, in the
+    fixed plan's order, and the tiles of a request do not depend on the rest
+    of the batch."""
+    L = np.full(10, 64 * 8, dtype=np.int64)          # every request: two 4-page tiles
+    t, ip = oracle.plan_fixed_packed(L, 4, 20, 128)
+    tf, ipf = oracle.plan_fixed(L, 4, 20)
+    assert np.array_equal(ip, ipf)
+    assert np.array_equal(t[:, :6], tf[:, :6]) and np.all(t[:, 6] == 4)
+    for name in ("dsv3", "verify"):
+        lens = workload_seq_lens(name)
+        t, ip = oracle.plan_fixed_packed(lens, 16, 256, CONFIGS[name]["heads"] * CONFIGS[name]["q_len"])
+        sub = lens[5:9]
+        t2, ip2 = oracle.plan_fixed_packed(sub, 16, 3, 128)
+        assert np.array_equal(np.diff(ip)[5:9], np.diff(ip2))
+
+
+@pytest.mark.parametrize("what", ["drop", "overlap", "tile", "field6", "order", "cost"])
+def test_check_fixed_packed_plan_rejects_broken_plans(what):
+    L = [130, 64, 300, 4000]
+    t, ip = oracle.plan_fixed_packed(L, 8, 5, 128)
+    t = t.copy()
+    if what == "drop":
+        t[4, 3] = 60; t[4, 5] = 12          # lose the last 3 pages
+    elif what == "overlap":
+        t[2, 1] = 8; t[2, 4] = 1; t[2, 5] = 24
+    elif what == "tile":
+        t[2, 4] = 1                          # wrong tile index for page 16
+    elif what == "field6":
+        t[1, 6] = 4
+    elif what == "order":
+        t[[1, 2]] = t[[2, 1]]
+    elif what == "cost":
+        # part 0 takes everything up to page 40 of the last request (292 > 128)
+        t[0] = [0, 0, 3, 40, 0, 49, 8, 0]; t[1] = 0; t[2] = 0; t[3] = [3, 40, 3, 48, 5, 8, 8, 0]
+    with pytest.raises(AssertionError):
+        oracle.check_fixed_packed_plan(t, ip, L, 8, 5, 128)
