@@ -442,6 +442,8 @@ mla_decode_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv
         constexpr int kLd = kCPrefix + 2;      // bf16 loads 9..17: slots 11, 14, .., 35
         constexpr int kM1 = kCLastScore + 1;   // max(1): slots 59..63
         constexpr int kW1 = kM1 + 5;           // tile 1, keys 0..7: slots 64..67
+        // (kW1 + 4 == kCSlots: the last branch of pay_c takes every slot from kW1
+        // on, so slots past the fourth would weigh keys 8..15 of tile 1 twice)
         static_assert(kE0 + 4 == kCPrefix && kCPrefix == kCFirstOut && kE1 + 6 * 3 < kCOutU1 &&
                           kW1 + 4 == kCSlots,
                       "combined chain payload layout");

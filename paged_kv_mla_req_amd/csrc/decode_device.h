@@ -592,9 +592,12 @@ __host__ __device__ constexpr bool cs_layout_ok() {
 }
 static_assert(cs_layout_ok() && kCSlots % 2 == 0,
               "combined chain: 36 score slots, waits within lgkmcnt range");
-constexpr int kCLastScore = cs_slot_of(true, kKSteps - 1);  // 54
-constexpr int kCFirstOut = cs_slot_of(false, 0);            // 13
-constexpr int kCOutU1 = cs_slot_of(false, kVTiles);         // 48: first MFMA on keys 16..31
+constexpr int kCLastScore = cs_slot_of(true, kKSteps - 1);  // 58
+constexpr int kCFirstOut = cs_slot_of(false, 0);            // 9
+// 43: the first output MFMA on keys 8..15 of each lane half (weights pop[1])
+constexpr int kCOutU1 = cs_slot_of(false, kVTiles);
+static_assert(kCLastScore == 58 && kCFirstOut == 9 && kCOutU1 == 43,
+              "the page loop's payload slots are placed for this layout");
 
 struct COps {
   bf16x8 k[kCSlots];            // score slots
